@@ -1,0 +1,246 @@
+/*
+ * sshdp.h -- C ABI of libsshdp.so: one GPU's share of the SS-HSDP update phase
+ * on MI355X (gfx950).
+ *
+ * Sources, cited by title and section:
+ *   [SS-HSDP]  "SS-HSDP: Efficient and Flexible Sharded Data Parallelism via
+ *              Runtime-Update Decoupling" (arXiv:2611.16467v1)
+ *   [OCP-MX]   OCP Microscaling Formats (MX) v1.0, the MXFP format cited there
+ *
+ * What the library computes.  [SS-HSDP §2.1]: an optimizer update F maps
+ * (main weight, main gradient, optimizer state) to new main weight and state,
+ * and weight preparation G casts or quantises the main weight into the
+ * low-precision runtime weight and its scales.  [SS-HSDP §3.1, EG1]: for Muon,
+ * F = [f0, f1, f2] per update unit (one attention head, one matrix): f0 updates
+ * the momentum and writes a BF16 intermediate u, f1 runs Newton-Schulz on u and
+ * produces an FP32 direction v, f2 updates the main weight from v; G produces
+ * FP8 (E4M3) weights with UE8M0 scales, and the weight transform Tw packs the
+ * head weights into the runtime weight (a view, no copy [SS-HSDP §3.2, §4.2])
+ * and relays the scales out for the GEMM kernel.  [SS-HSDP §5.2]: AdamW updates
+ * the parameters Muon does not.
+ *
+ * Data model.  Every field (main weight, gradient, momentum, AdamW second
+ * moment, FP8 codes) is ONE flat root allocation indexed by the same element
+ * offsets; views are described by a data tree [SS-HSDP §3.2 "Data Tree"]: a
+ * child is a view at an element offset inside its parent, only the root owns
+ * storage.  Codes mirror the fp32 root byte-for-element, so a head's codes are a
+ * sub-range of its packed projection's codes.  Scales are one byte per 32
+ * elements, in one of two layouts (see SSHDP_SCALE_*).
+ *
+ * Conventions.  All functions return an int status: SSHDP_OK (0) or a negative
+ * SSHDP_ERR_* code; sshdp_status_string() names it.  Device pointers are
+ * caller-owned, must stay valid until the enqueued work has run, and must be
+ * 16-byte aligned.  `stream` is a hipStream_t passed as void* (NULL = the
+ * default stream); every launching call is asynchronous on it, performs no
+ * allocation and no synchronisation.  Plans are immutable after creation; calls
+ * on different streams with different workspaces may overlap, calls sharing a
+ * workspace are serialised by the caller's stream order.  The library keeps no
+ * state between calls: the step counter is an argument.
+ */
+#ifndef SSHDP_H
+#define SSHDP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSHDP_ABI_VERSION 1
+
+/* Status codes.  The planning errors are the rejections of [SS-HSDP Appendix A,
+ * Table 4]: incompatible metadata, invalid geometry, storage overlap. */
+enum {
+  SSHDP_OK = 0,
+  SSHDP_ERR_ARG = -1,       /* null pointer, empty table, step < 1, bad option value   */
+  SSHDP_ERR_TREE = -2,      /* a parent index is not an earlier node                   */
+  SSHDP_ERR_BOUNDS = -3,    /* a view leaves its parent or the root                    */
+  SSHDP_ERR_OVERLAP = -4,   /* two units, or two quantised regions, share an element   */
+  SSHDP_ERR_SCHEMA = -5,    /* geometry/metadata the kernels cannot take (see below)   */
+  SSHDP_ERR_ALIGN = -6,     /* a device pointer is not 16-byte aligned                 */
+  SSHDP_ERR_WORKSPACE = -7, /* workspace missing or smaller than sshdp_plan_info says  */
+  SSHDP_ERR_HIP = -8,       /* a HIP runtime call or kernel launch failed              */
+  SSHDP_ERR_STATE = -9      /* the plan was made host-only and cannot launch           */
+};
+
+enum { SSHDP_OPT_NONE = 0, SSHDP_OPT_MUON = 1, SSHDP_OPT_ADAMW = 2 };
+
+/* Scale layouts.  For a quantised region at absolute element offset o with N
+ * rows and K columns (KB = K/32 blocks per row), the scale of block (n, kb):
+ *   ROWMAJOR : o/32 + n*KB + kb             (= index of its first element / 32)
+ *   TILE32X4 : o/32 + ((n/32)*(KB/4) + kb/4)*128 + (n%32)*4 + kb%4
+ * TILE32X4 stores each 32-row x 128-column tile's scales as one 128-byte run,
+ * one 4-byte word per row holding 4 consecutive K-blocks: the operand a 32-row
+ * scaled-MFMA tile reads in one coalesced load.  It is this library's own
+ * layout (the [SS-HSDP] kernels' layout belongs to other hardware).  Both
+ * layouts keep a head's scales a sub-range of its projection's when the head's
+ * row count is a multiple of 32. */
+enum { SSHDP_SCALE_ROWMAJOR = 0, SSHDP_SCALE_TILE32X4 = 1 };
+
+/* Plan flags. */
+enum {
+  SSHDP_PLAN_HOST_ONLY = 1  /* plan and validate on the host; no device tables (cannot launch) */
+};
+
+/* One data-tree node [SS-HSDP §3.2]: a 2-D view (rows x cols, cols contiguous,
+ * rows `row_stride` elements apart) at `offset` elements from its parent's first
+ * element.  A 1-D tensor is rows = 1.  `is_unit` marks an update parameter (a
+ * leaf of the optimisation [SS-HSDP §3.1]) with `optimizer` SSHDP_OPT_MUON or
+ * SSHDP_OPT_ADAMW; `quantize` marks a region (a runtime weight, or a unit) that
+ * G requantises to MXFP8.  Rules (else the error named):
+ *   parent is -1 or an earlier node index                          (TREE)
+ *   rows, cols >= 1, offset >= 0, row_stride >= cols if rows > 1   (SCHEMA)
+ *   the view lies inside its parent's extent and the root           (BOUNDS)
+ *   a Muon unit is 2-D (rows, cols >= 2) and its first element, row_stride
+ *     and cols are multiples of 4 (16-byte vectors)                (SCHEMA)
+ *   a quantised region is contiguous (row_stride == cols), with cols and its
+ *     first element multiples of 32; for TILE32X4 also rows % 32 == 0 and
+ *     cols % 128 == 0                                               (SCHEMA)
+ *   units are pairwise disjoint; quantised regions too             (OVERLAP)
+ * Checks run node by node in index order; overlap is checked last. */
+typedef struct {
+  int32_t parent;
+  int32_t is_unit;
+  int64_t offset;
+  int64_t rows;
+  int64_t cols;
+  int64_t row_stride;
+  int32_t optimizer;
+  int32_t quantize;
+} sshdp_node;
+
+/* Plan options.  Defaults (sshdp_default_opts): 5 Newton-Schulz steps with
+ * (a, b, c) = (3.4445, -4.7750, 2.0315) on the Frobenius-normalised u, ns_eps =
+ * 1e-7 added to the norm, heavy-ball momentum (nesterov = 0), update scale mode
+ * 0 (scale 1; mode 1: sqrt(max(1, rows/cols)); mode 2: 0.2*sqrt(max(rows,
+ * cols))), ROWMAJOR scales, flags 0. */
+typedef struct {
+  int32_t ns_steps;
+  float ns_a, ns_b, ns_c;
+  float ns_eps;
+  int32_t scale_layout;
+  int32_t nesterov;
+  int32_t muon_scale_mode;
+  uint32_t flags;
+} sshdp_plan_opts;
+
+/* Muon: m <- momentum*m + g; u = bf16(m) (nesterov: bf16(g + momentum*m));
+ * v = NS(u); w <- w - lr*weight_decay*w - lr*scale*v. */
+typedef struct { float lr, momentum, weight_decay; } sshdp_muon_hp;
+
+/* AdamW: w <- w - lr*wd*w; m <- b1 m + (1-b1) g; v <- b2 v + (1-b2) g^2;
+ * w <- w - lr * (m/(1-b1^t)) / (sqrt(v/(1-b2^t)) + eps). */
+typedef struct { float lr, beta1, beta2, eps, weight_decay; } sshdp_adamw_hp;
+
+/* Caller-owned device roots, all indexed by the same element offsets.
+ * w_main, grad, mom (Muon momentum and AdamW first moment): fp32, root_numel
+ * elements.  adam_v: fp32 root or NULL when the plan has no AdamW units.
+ * codes: uint8 root of root_numel bytes (E4M3FN).  scales: uint8, at least
+ * sshdp_plan_stats.scale_bytes bytes (E8M0).  Only unit elements of w_main,
+ * mom, adam_v and quantised-region bytes of codes/scales are written. */
+typedef struct {
+  float *w_main;
+  const float *grad;
+  float *mom;
+  float *adam_v;
+  uint8_t *codes;
+  uint8_t *scales;
+} sshdp_buffers;
+
+typedef struct sshdp_plan sshdp_plan;   /* opaque; owns host tables and one device table block */
+
+/* Figures a caller needs to size buffers, and the algorithmic work per step. */
+typedef struct {
+  int64_t root_numel;
+  int64_t scale_bytes;        /* bytes of the scale root: ceil(root_numel / 32)            */
+  int64_t workspace_bytes;    /* device workspace sshdp_update_muon/_step need (256-aligned) */
+  int32_t n_nodes, n_units, n_muon_units, n_adamw_units, n_quant_regions, n_groups;
+  int64_t muon_elems, adamw_elems, quant_elems;
+  int64_t fused_quant_elems;  /* quantised elements G handles inside the AdamW pass       */
+  double ns_flops;            /* 5*(4 r^2 c + 2 r^3)-style dense count over all Muon units */
+} sshdp_plan_stats;
+
+/* One Newton-Schulz batch: the Muon units sharing an oriented shape r x c
+ * (r = min(rows, cols)), run as one batched GEMM per stage [SS-HSDP §4.1]. */
+typedef struct {
+  int32_t r, c;               /* oriented shape                                            */
+  int32_t r_pad, c_pad;       /* padded to the GEMM tile                                   */
+  int32_t n_units;
+  int32_t tile;               /* GEMM macro-tile edge used for this group                  */
+} sshdp_group_info;
+
+/* Fill *opts with the defaults above. */
+int sshdp_default_opts(sshdp_plan_opts *opts);
+
+/* Resolve the data tree and build a plan [SS-HSDP §3.2 "Data Tree"; §3.3
+ * groups; Appendix A Table 4 rejections].  Host-synchronous; unless
+ * SSHDP_PLAN_HOST_ONLY, allocates and uploads one block of device descriptor
+ * tables on the current HIP device.  Errors leave *out_plan NULL and touch no
+ * device memory.  The plan is freed by sshdp_plan_destroy. */
+int sshdp_plan_views(const sshdp_node *nodes, int32_t n_nodes, int64_t root_numel,
+                     const sshdp_plan_opts *opts, sshdp_plan **out_plan);
+
+int sshdp_plan_info(const sshdp_plan *plan, sshdp_plan_stats *stats);
+int sshdp_plan_group(const sshdp_plan *plan, int32_t group, sshdp_group_info *info);
+/* Absolute element offset of node `node` (accumulated along its chain) and the
+ * Newton-Schulz group of a Muon unit (-1 otherwise). */
+int sshdp_plan_node(const sshdp_plan *plan, int32_t node, int64_t *abs_offset, int32_t *group);
+void sshdp_plan_destroy(sshdp_plan *plan);
+
+/* F for every Muon unit: f0 (momentum, bf16 u, ||u||^2), f1 (Newton-Schulz,
+ * batched bf16 MFMA GEMMs per group) and f2 (main-weight update, fused into the
+ * last Newton-Schulz product) [SS-HSDP §3.1 EG1, §4.1].  Reads grad, mom,
+ * w_main; writes mom, w_main.  `workspace`: device memory of at least
+ * stats.workspace_bytes, 256-byte aligned; its contents on entry are ignored. */
+int sshdp_update_muon(const sshdp_plan *plan, const sshdp_buffers *bufs, const sshdp_muon_hp *hp,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* F for every AdamW unit at step `step` (>= 1, caller-owned, same for all
+ * units).  Reads grad, mom, adam_v, w_main; writes mom, adam_v, w_main. */
+int sshdp_update_adamw(const sshdp_plan *plan, const sshdp_buffers *bufs, const sshdp_adamw_hp *hp,
+                       int64_t step, void *stream);
+
+/* G + the scale part of Tw for every quantised region [SS-HSDP §3.1 EG1; OCP-MX]:
+ * per 1x32 block along K, e = least integer with amax <= 448*2^e (clamped to
+ * [-127,127]; all-zero block -> -127), scale byte e+127 at the layout's index,
+ * codes = E4M3FN round-to-nearest-even of x*2^-e, written at the elements' own
+ * offsets.  A block holding NaN/Inf gets scale 0xFF and codes 0x7F.  Reads
+ * w_main; writes codes and scales. */
+int sshdp_requant_mxfp8(const sshdp_plan *plan, const float *w_main, uint8_t *codes, uint8_t *scales,
+                        void *stream);
+
+/* The whole update phase in order [SS-HSDP §3.4 "Update"]: Muon F, AdamW F
+ * (fused with G for quantised regions holding only AdamW units), then G for the
+ * remaining quantised regions.  Equivalent to sshdp_update_muon;
+ * sshdp_update_adamw; sshdp_requant_mxfp8. */
+int sshdp_update_step(const sshdp_plan *plan, const sshdp_buffers *bufs, const sshdp_muon_hp *mh,
+                      const sshdp_adamw_hp *ah, int64_t step, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* Diagnostics.  The batched NT contraction used by Newton-Schulz, exposed to
+ * test it alone: for b < batch, O[b] = bf16(alpha * P[b] Q[b]^T + beta * D[b])
+ * with P[b] M x K, Q[b] N x K, D[b], O[b] M x N (bf16, row-major, dense, batch
+ * strides M*K, N*K, M*N); OT (optional) receives O[b]^T (N x M).  M, N must be
+ * multiples of `tile` (64, 128 or 256), K of 64; D may be NULL (beta ignored). */
+int sshdp_gemm_bf16_nt(const void *P, const void *Q, const void *D, void *O, void *OT, int32_t M,
+                       int32_t N, int32_t K, int32_t batch, float alpha, float beta, int32_t tile,
+                       void *stream);
+
+/* Per-stage kernel timing for benchmarking: when enabled on a plan, launching
+ * calls bracket each kernel class with HIP events on the launch stream and
+ * accumulate durations (milliseconds) and launch counts; reading synchronises
+ * on those events.  Classes: 0 momentum (f0), 1 norm, 2 NS Gram, 3 NS poly,
+ * 4 NS update (+f2), 5 AdamW, 6 AdamW+G fused, 7 G requant.  Not thread-safe;
+ * for measurement only. */
+enum { SSHDP_PROF_CLASSES = 8 };
+int sshdp_profile_enable(sshdp_plan *plan, int32_t enable);
+int sshdp_profile_read(sshdp_plan *plan, double *ms, int64_t *launches);
+
+const char *sshdp_status_string(int code);
+int sshdp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSHDP_H */

@@ -1,0 +1,233 @@
+// api.hip -- the launching entry points of libsshdp.so.
+//
+// [SS-HSDP §3.4 "Update"]: after the microbatches each unit's F runs (Muon:
+// f0 local momentum, f1 Newton-Schulz on the whole unit, f2 local weight
+// update), AdamW runs for the remaining units, and applying G to the updated
+// main weights begins the next cycle.  [SS-HSDP Appendix A]: stages run in
+// order within an update group, each consuming the committed outputs of the
+// previous; here that order is the order of launches on one stream.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+using namespace sshdp;
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SSHDP_OK : SSHDP_ERR_HIP; }
+
+int check_plan(const sshdp_plan *p) {
+  if (!p) return SSHDP_ERR_ARG;
+  if (p->host_only) return SSHDP_ERR_STATE;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return SSHDP_ERR_HIP;
+  if (cur != p->device) return SSHDP_ERR_ARG;
+  return SSHDP_OK;
+}
+
+// Event bracketing of one kernel class (measurement only).
+struct Prof {
+  sshdp_plan *p;
+  int cls;
+  hipStream_t s;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  Prof(const sshdp_plan *pl, int c, hipStream_t st) : p(const_cast<sshdp_plan *>(pl)), cls(c), s(st) {
+    if (!p->prof) return;
+    e0 = take();
+    e1 = take();
+    if (e0) hipEventRecord(e0, s);
+  }
+  ~Prof() {
+    if (!p->prof || !e0 || !e1) return;
+    hipEventRecord(e1, s);
+    p->prof_pending.push_back({cls, {e0, e1}});
+  }
+  hipEvent_t take() {
+    if (!p->prof_pool.empty()) {
+      hipEvent_t e = p->prof_pool.back();
+      p->prof_pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+
+int run_muon(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_muon_hp *hp, void *ws, size_t ws_bytes,
+             hipStream_t s) {
+  if (p->munits.empty()) return SSHDP_OK;
+  if (!b->w_main || !b->grad || !b->mom) return SSHDP_ERR_ARG;
+  if (!aligned16(b->w_main) || !aligned16(b->grad) || !aligned16(b->mom)) return SSHDP_ERR_ALIGN;
+  if (!ws || ws_bytes < p->ws_bytes) return SSHDP_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) return SSHDP_ERR_ALIGN;
+  char *w = static_cast<char *>(ws);
+  hipError_t e;
+  {
+    Prof pr(p, 0, s);
+    e = launch_f0(*p, b->grad, b->mom, hp->momentum, p->opts.nesterov, w, s);
+  }
+  if (e != hipSuccess) return SSHDP_ERR_HIP;
+  {
+    Prof pr(p, 1, s);
+    e = launch_norm(*p, w, p->opts.ns_eps, s);
+  }
+  if (e != hipSuccess) return SSHDP_ERR_HIP;
+  const int steps = p->opts.ns_steps;
+  for (int it = 0; it < steps; ++it) {
+    for (const Group &g : p->groups) {
+      {
+        Prof pr(p, 2, s);
+        e = launch_ns_stage(*p, g, 0, it, w, b->w_main, hp->lr, hp->weight_decay, s);
+      }
+      if (e != hipSuccess) return SSHDP_ERR_HIP;
+      {
+        Prof pr(p, 3, s);
+        e = launch_ns_stage(*p, g, 1, it, w, b->w_main, hp->lr, hp->weight_decay, s);
+      }
+      if (e != hipSuccess) return SSHDP_ERR_HIP;
+      {
+        Prof pr(p, 4, s);
+        e = launch_ns_stage(*p, g, it + 1 == steps ? 3 : 2, it, w, b->w_main, hp->lr, hp->weight_decay, s);
+      }
+      if (e != hipSuccess) return SSHDP_ERR_HIP;
+    }
+  }
+  return SSHDP_OK;
+}
+
+int check_adam(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_adamw_hp *hp, int64_t step) {
+  if (!hp || step < 1) return SSHDP_ERR_ARG;
+  if (!b->w_main || !b->grad || !b->mom || !b->adam_v) return SSHDP_ERR_ARG;
+  if (!aligned16(b->w_main) || !aligned16(b->grad) || !aligned16(b->mom) || !aligned16(b->adam_v))
+    return SSHDP_ERR_ALIGN;
+  (void)p;
+  return SSHDP_OK;
+}
+
+int check_quant(const float *w, const uint8_t *codes, const uint8_t *scales) {
+  if (!w || !codes || !scales) return SSHDP_ERR_ARG;
+  if (!aligned16(w) || !aligned16(codes)) return SSHDP_ERR_ALIGN;
+  return SSHDP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sshdp_update_muon(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_muon_hp *hp, void *ws,
+                      size_t ws_bytes, void *stream) {
+  int st = check_plan(p);
+  if (st != SSHDP_OK) return st;
+  if (!b || !hp) return SSHDP_ERR_ARG;
+  return run_muon(p, b, hp, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int sshdp_update_adamw(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_adamw_hp *hp, int64_t step,
+                       void *stream) {
+  int st = check_plan(p);
+  if (st != SSHDP_OK) return st;
+  if (!b) return SSHDP_ERR_ARG;
+  if (p->aseg_all.empty()) return (hp && step >= 1) ? SSHDP_OK : SSHDP_ERR_ARG;
+  st = check_adam(p, b, hp, step);
+  if (st != SSHDP_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Prof pr(p, 5, s);
+  return hip_status(launch_adamw(p->d.aseg_all, (int64_t)p->aseg_all.size(), *b, *hp, step, s));
+}
+
+int sshdp_requant_mxfp8(const sshdp_plan *p, const float *w_main, uint8_t *codes, uint8_t *scales, void *stream) {
+  int st = check_plan(p);
+  if (st != SSHDP_OK) return st;
+  if (p->qchunks.empty()) return SSHDP_OK;
+  st = check_quant(w_main, codes, scales);
+  if (st != SSHDP_OK) return st;
+  sshdp_buffers b{};
+  b.w_main = const_cast<float *>(w_main);
+  b.codes = codes;
+  b.scales = scales;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Prof pr(p, 7, s);
+  return hip_status(launch_quant(*p, 0, (int64_t)p->qchunks.size(), false, b, nullptr, 1, s));
+}
+
+int sshdp_update_step(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_muon_hp *mh,
+                      const sshdp_adamw_hp *ah, int64_t step, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_plan(p);
+  if (st != SSHDP_OK) return st;
+  if (!b) return SSHDP_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!p->munits.empty() && !mh) return SSHDP_ERR_ARG;
+  if (!p->aseg_all.empty()) {
+    st = check_adam(p, b, ah, step);
+    if (st != SSHDP_OK) return st;
+  } else if (step < 1) {
+    return SSHDP_ERR_ARG;
+  }
+  if (!p->qchunks.empty()) {
+    st = check_quant(b->w_main, b->codes, b->scales);
+    if (st != SSHDP_OK) return st;
+  }
+  if (!p->munits.empty()) {
+    st = run_muon(p, b, mh, ws, ws_bytes, s);
+    if (st != SSHDP_OK) return st;
+  }
+  if (!p->aseg_unfused.empty()) {
+    Prof pr(p, 5, s);
+    st = hip_status(launch_adamw(p->d.aseg_unfused, (int64_t)p->aseg_unfused.size(), *b, *ah, step, s));
+  }
+  if (st != SSHDP_OK) return st;
+  if (p->n_qchunks_fused > 0) {
+    Prof pr(p, 6, s);
+    st = hip_status(launch_quant(*p, 0, p->n_qchunks_fused, true, *b, ah, step, s));
+  }
+  if (st != SSHDP_OK) return st;
+  const int64_t rest = (int64_t)p->qchunks.size() - p->n_qchunks_fused;
+  if (rest > 0) {
+    Prof pr(p, 7, s);
+    st = hip_status(launch_quant(*p, p->n_qchunks_fused, rest, false, *b, nullptr, step, s));
+  }
+  return st;
+}
+
+int sshdp_gemm_bf16_nt(const void *P, const void *Q, const void *D, void *O, void *OT, int32_t M, int32_t N,
+                       int32_t K, int32_t batch, float alpha, float beta, int32_t tile, void *stream) {
+  if (!P || !Q || !O || M <= 0 || N <= 0 || K <= 0 || batch <= 0) return SSHDP_ERR_ARG;
+  if (tile != 128 && tile != 256) return SSHDP_ERR_ARG;
+  if (M % tile || N % tile || K % 64) return SSHDP_ERR_SCHEMA;
+  if (!aligned16(P) || !aligned16(Q) || (D && !aligned16(D)) || !aligned16(O) || (OT && !aligned16(OT)))
+    return SSHDP_ERR_ALIGN;
+  return hip_status(launch_gemm_raw(P, Q, D, O, OT, M, N, K, batch, alpha, D ? beta : 0.f, tile,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int sshdp_profile_enable(sshdp_plan *p, int32_t enable) {
+  if (!p) return SSHDP_ERR_ARG;
+  p->prof = enable != 0;
+  return SSHDP_OK;
+}
+
+int sshdp_profile_read(sshdp_plan *p, double *ms, int64_t *launches) {
+  if (!p) return SSHDP_ERR_ARG;
+  for (auto &e : p->prof_pending) {
+    if (hipEventSynchronize(e.second.second) != hipSuccess) return SSHDP_ERR_HIP;
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, e.second.first, e.second.second) != hipSuccess) return SSHDP_ERR_HIP;
+    p->prof_ms[e.first] += t;
+    p->prof_n[e.first] += 1;
+    p->prof_pool.push_back(e.second.first);
+    p->prof_pool.push_back(e.second.second);
+  }
+  p->prof_pending.clear();
+  for (int i = 0; i < SSHDP_PROF_CLASSES; ++i) {
+    if (ms) ms[i] = p->prof_ms[i];
+    if (launches) launches[i] = p->prof_n[i];
+    p->prof_ms[i] = 0.0;
+    p->prof_n[i] = 0;
+  }
+  return SSHDP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,123 @@
+// internal.h -- plan tables shared by the host planner and the HIP kernels.
+#pragma once
+#include <stdint.h>
+#include <stddef.h>
+
+#include <vector>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/sshdp.h"
+
+namespace sshdp {
+
+constexpr int kF0Tile = 64;          // f0 transposing tile edge (elements)
+constexpr int kChunk = 4096;         // elements per AdamW / requant work item
+constexpr size_t kAlign = 256;       // workspace sub-buffer alignment (bytes)
+
+// One Muon unit as the kernels see it (device table, ordered by group).
+struct MuonUnit {
+  int64_t abs;          // absolute element offset of element (0,0) in the roots
+  int64_t row_stride;   // elements between rows of the original view
+  int32_t rows, cols;   // original view shape
+  int32_t tall;         // rows > cols: oriented matrix X is the transpose of the view
+  int32_t group;        // Newton-Schulz group
+  int32_t idx;          // position inside the group (GEMM batch index)
+  int32_t tile_begin;   // f0 tiles [tile_begin, tile_end) -> norm partials
+  int32_t tile_end;
+  int32_t Rp, Cp;       // padded original dims: the unit's own layout is Rp x Cp
+  int64_t ws_orig;      // workspace byte offset of bf16 u in the unit's own layout (Rp x Cp)
+  int64_t ws_trans;     // ... and of its transpose (Cp x Rp)
+  float upd_scale;      // update scale (scale mode) of f2
+  int32_t pad_;
+};
+
+// One f0 tile: a kF0Tile x kF0Tile block of the unit's original (padded) layout.
+struct F0Tile {
+  int32_t unit;
+  int32_t tr, tc;       // tile row / column index
+};
+
+// Newton-Schulz group: units with the same oriented shape r x c (r <= c).
+struct Group {
+  int32_t r, c, r_pad, c_pad, n, tile;
+  int32_t unit_base;    // first MuonUnit of the group in the device table
+  size_t off_x, off_xt0, off_xt1, off_a, off_b;   // workspace byte offsets
+};
+
+// AdamW work item: a contiguous run of unit elements (<= kChunk).
+struct ASeg {
+  int64_t base;
+  int32_t n;
+  int32_t pad_;
+};
+
+// Quantised region (runtime weight or quantised unit); contiguous, 32-aligned.
+struct QRegion {
+  int64_t abs;
+  int64_t rows;
+  int32_t cols;
+  int32_t pad_;
+};
+
+// Requant work item: blocks [base, base + n) of one region (n % 32 == 0,
+// n <= kChunk); elements in [lo, hi) are AdamW-updated first when fused.
+struct QChunk {
+  int64_t base;
+  int64_t lo, hi;
+  int32_t n;
+  int32_t region;
+};
+
+struct DeviceTables {
+  MuonUnit *munits = nullptr;
+  F0Tile *f0tiles = nullptr;
+  ASeg *aseg_all = nullptr;
+  ASeg *aseg_unfused = nullptr;
+  QRegion *qregions = nullptr;
+  QChunk *qchunks = nullptr;
+};
+
+}  // namespace sshdp
+
+struct sshdp_plan {
+  int64_t root_numel = 0;
+  sshdp_plan_opts opts{};
+  std::vector<int64_t> node_abs;
+  std::vector<int32_t> node_group;
+  std::vector<sshdp::MuonUnit> munits;
+  std::vector<sshdp::F0Tile> f0tiles;
+  std::vector<sshdp::Group> groups;
+  std::vector<sshdp::ASeg> aseg_all, aseg_unfused;
+  std::vector<sshdp::QRegion> qregions;
+  std::vector<sshdp::QChunk> qchunks;   // fused-eligible chunks first
+  int64_t n_qchunks_fused = 0;
+  size_t ws_uscale = 0, ws_partials = 0, ws_bytes = 0;
+  sshdp_plan_stats stats{};
+  bool host_only = true;
+  int device = -1;
+  void *dblock = nullptr;
+  sshdp::DeviceTables d;
+  // measurement
+  bool prof = false;
+  double prof_ms[SSHDP_PROF_CLASSES] = {};
+  int64_t prof_n[SSHDP_PROF_CLASSES] = {};
+  std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> prof_pending;
+  std::vector<hipEvent_t> prof_pool;
+};
+
+// Kernel launchers (defined in the .hip translation units).
+namespace sshdp {
+hipError_t launch_f0(const sshdp_plan &p, const float *g, float *m, float mu, int nesterov, char *ws,
+                     hipStream_t s);
+hipError_t launch_norm(const sshdp_plan &p, char *ws, float eps, hipStream_t s);
+// stage: 0 Gram, 1 poly, 2 update, 3 final update (+f2)
+hipError_t launch_ns_stage(const sshdp_plan &p, const Group &g, int stage, int iter, char *ws,
+                           float *w_main, float lr, float wd, hipStream_t s);
+hipError_t launch_gemm_raw(const void *P, const void *Q, const void *D, void *O, void *OT, int M, int N,
+                           int K, int batch, float alpha, float beta, int tile, hipStream_t s);
+hipError_t launch_adamw(const ASeg *segs, int64_t nseg, const sshdp_buffers &b, const sshdp_adamw_hp &hp,
+                        int64_t step, hipStream_t s);
+hipError_t launch_quant(const sshdp_plan &p, int64_t first, int64_t count, bool fused, const sshdp_buffers &b,
+                        const sshdp_adamw_hp *hp, int64_t step, hipStream_t s);
+}  // namespace sshdp

@@ -1,0 +1,314 @@
+// k_elementwise.hip -- the HBM-streaming stages of the update phase on gfx950:
+//   f0   Muon momentum + bf16 u (own layout and transposed) + ||u||^2 partials
+//   norm per-unit 1 / (||u||_F + eps), deterministic reduction of the partials
+//   AdamW for elementwise units
+//   G    MXFP8 requantisation (1x32 blocks along K), optionally fused with AdamW
+//
+// [SS-HSDP §3.1 EG1]: f0 updates the momentum from the gradient and writes a
+// BF16 intermediate u; G quantises the main weight to FP8 with UE8M0 scales and
+// Tw relays the scales out for the GEMM.  [SS-HSDP §4.1]: the elementwise
+// stages run as multi-tensor kernels over all units in one launch.  [OCP-MX]:
+// one E8M0 scale per 32-element block, E4M3 elements.
+//
+// Memory access: every global access is a 16-byte vector per lane with
+// consecutive lanes on consecutive addresses (8 lanes = one 128-byte MX block);
+// block amax is an 8-lane butterfly over the lanes holding the block.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "internal.h"
+#include "mx_codec.h"
+
+namespace sshdp {
+namespace {
+
+__device__ __forceinline__ uint32_t fbits(float x) { return __float_as_uint(x); }
+
+// ----------------------------------------------------------------------------- f0
+// One 64x64 tile of a Muon unit's own (padded) layout per workgroup of 256.
+// Elements outside the unit write u = 0 (the padding the GEMMs rely on).
+__global__ __launch_bounds__(256) void k_f0(const MuonUnit *__restrict__ units, const F0Tile *__restrict__ tiles,
+                                            const float *__restrict__ g, float *__restrict__ m, float mu,
+                                            int nesterov, char *__restrict__ ws, float *__restrict__ partials) {
+  constexpr int T = kF0Tile, PITCH = T + 8;          // bf16 elements; rows 16-byte aligned
+  __shared__ uint16_t lds[T * PITCH];
+  __shared__ float red[4];
+  const F0Tile tl = tiles[blockIdx.x];
+  const MuonUnit u = units[tl.unit];
+  const int t = threadIdx.x;
+  const int cq = t & 15, r0 = t >> 4;
+  const int col = tl.tc * T + cq * 4;
+  uint16_t *orig = reinterpret_cast<uint16_t *>(ws + u.ws_orig);
+  uint16_t *trans = reinterpret_cast<uint16_t *>(ws + u.ws_trans);
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int lr = r0 + 16 * i;
+    const int row = tl.tr * T + lr;
+    uint32_t b[4] = {0u, 0u, 0u, 0u};
+    if (row < u.rows && col < u.cols) {
+      const int64_t e = u.abs + (int64_t)row * u.row_stride + col;
+      const float4 gv = *reinterpret_cast<const float4 *>(g + e);
+      float4 mv = *reinterpret_cast<const float4 *>(m + e);
+      mv.x = fmaf(mu, mv.x, gv.x);
+      mv.y = fmaf(mu, mv.y, gv.y);
+      mv.z = fmaf(mu, mv.z, gv.z);
+      mv.w = fmaf(mu, mv.w, gv.w);
+      *reinterpret_cast<float4 *>(m + e) = mv;
+      float4 src = mv;
+      if (nesterov) {
+        src.x = fmaf(mu, mv.x, gv.x);
+        src.y = fmaf(mu, mv.y, gv.y);
+        src.z = fmaf(mu, mv.z, gv.z);
+        src.w = fmaf(mu, mv.w, gv.w);
+      }
+      b[0] = mx_bf16_bits(fbits(src.x));
+      b[1] = mx_bf16_bits(fbits(src.y));
+      b[2] = mx_bf16_bits(fbits(src.z));
+      b[3] = mx_bf16_bits(fbits(src.w));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float q = __uint_as_float(b[j] << 16);
+        ss = fmaf(q, q, ss);
+      }
+    }
+    uint2 packed;
+    packed.x = b[0] | (b[1] << 16);
+    packed.y = b[2] | (b[3] << 16);
+    *reinterpret_cast<uint2 *>(orig + (int64_t)row * u.Cp + col) = packed;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lds[(cq * 4 + j) * PITCH + lr] = (uint16_t)b[j];
+  }
+  // sum of squares: wave butterfly, then the 4 waves in order (deterministic)
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  if (t == 0) partials[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+  // transposed tile: row c of the transpose = column c of the tile
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int c = (t >> 3) + 32 * pass, seg = t & 7;
+    const uint4 v = *reinterpret_cast<const uint4 *>(&lds[c * PITCH + seg * 8]);
+    *reinterpret_cast<uint4 *>(trans + (int64_t)(tl.tc * T + c) * u.Rp + tl.tr * T + seg * 8) = v;
+  }
+}
+
+// ----------------------------------------------------------------------------- norm
+__global__ __launch_bounds__(256) void k_norm(const MuonUnit *__restrict__ units, const float *__restrict__ partials,
+                                              float *__restrict__ uscale, float eps) {
+  __shared__ float red[4];
+  const MuonUnit u = units[blockIdx.x];
+  float s = 0.f;
+  for (int i = u.tile_begin + threadIdx.x; i < u.tile_end; i += 256) s += partials[i];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    uscale[blockIdx.x] = 1.0f / (sqrtf(tot) + eps);
+  }
+}
+
+// ----------------------------------------------------------------------------- AdamW
+struct AdamConst {
+  float lr, b1, b2, eps, decay;   // decay = 1 - lr*wd
+  float omb1, omb2, bc1, bc2;     // 1-b1, 1-b2, 1-b1^t, 1-b2^t
+};
+
+__device__ __forceinline__ void adam_elem(float &w, float g, float &m, float &v, const AdamConst &c) {
+  w = w * c.decay;
+  m = fmaf(c.b1, m, c.omb1 * g);
+  v = fmaf(c.b2, v, c.omb2 * (g * g));
+  const float mhat = m / c.bc1;
+  const float vhat = v / c.bc2;
+  w = w - c.lr * (mhat / (sqrtf(vhat) + c.eps));
+}
+
+__global__ __launch_bounds__(256) void k_adamw(const ASeg *__restrict__ segs, float *__restrict__ w,
+                                               const float *__restrict__ g, float *__restrict__ m,
+                                               float *__restrict__ v, AdamConst c) {
+  const ASeg s = segs[blockIdx.x];
+  const int t = threadIdx.x;
+  if ((s.base & 3) == 0) {
+    const int nv = s.n >> 2;
+    for (int i = t; i < nv; i += 256) {
+      const int64_t e = s.base + 4 * (int64_t)i;
+      float4 wv = *reinterpret_cast<const float4 *>(w + e);
+      const float4 gv = *reinterpret_cast<const float4 *>(g + e);
+      float4 mv = *reinterpret_cast<const float4 *>(m + e);
+      float4 vv = *reinterpret_cast<const float4 *>(v + e);
+      adam_elem(wv.x, gv.x, mv.x, vv.x, c);
+      adam_elem(wv.y, gv.y, mv.y, vv.y, c);
+      adam_elem(wv.z, gv.z, mv.z, vv.z, c);
+      adam_elem(wv.w, gv.w, mv.w, vv.w, c);
+      *reinterpret_cast<float4 *>(w + e) = wv;
+      *reinterpret_cast<float4 *>(m + e) = mv;
+      *reinterpret_cast<float4 *>(v + e) = vv;
+    }
+    for (int i = 4 * nv + t; i < s.n; i += 256) {
+      const int64_t e = s.base + i;
+      float wv = w[e], mv = m[e], vv = v[e];
+      adam_elem(wv, g[e], mv, vv, c);
+      w[e] = wv; m[e] = mv; v[e] = vv;
+    }
+  } else {
+    for (int i = t; i < s.n; i += 256) {
+      const int64_t e = s.base + i;
+      float wv = w[e], mv = m[e], vv = v[e];
+      adam_elem(wv, g[e], mv, vv, c);
+      w[e] = wv; m[e] = mv; v[e] = vv;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- G (+ AdamW)
+// One chunk (<= kChunk elements, whole 32-blocks) per workgroup; four passes of
+// 1024 elements, each lane owning 4 consecutive elements, 8 lanes per block.
+// All loads of a chunk are issued before any arithmetic.
+template <bool FUSED>
+__global__ __launch_bounds__(256) void k_quant(const QChunk *__restrict__ chunks, const QRegion *__restrict__ regions,
+                                               int tile_layout, float *__restrict__ w, const float *__restrict__ g,
+                                               float *__restrict__ m, float *__restrict__ v,
+                                               uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                               AdamConst c) {
+  constexpr int P = kChunk / 1024;
+  const QChunk q = chunks[blockIdx.x];
+  const int t = threadIdx.x;
+  float4 wv[P], gv[P], mv[P], vv[P];
+  bool live[P], upd[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) wv[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int off = p * 1024 + 4 * t;
+    const int64_t e = q.base + off;
+    live[p] = off < q.n;
+    upd[p] = FUSED && live[p] && e + 4 > q.lo && e < q.hi;
+    if (live[p]) wv[p] = *reinterpret_cast<const float4 *>(w + e);
+    if (upd[p]) {
+      gv[p] = *reinterpret_cast<const float4 *>(g + e);
+      mv[p] = *reinterpret_cast<const float4 *>(m + e);
+      vv[p] = *reinterpret_cast<const float4 *>(v + e);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int64_t e = q.base + p * 1024 + 4 * t;
+    if (FUSED && upd[p]) {
+      float *wp = reinterpret_cast<float *>(&wv[p]);
+      const float *gp = reinterpret_cast<const float *>(&gv[p]);
+      float *mp = reinterpret_cast<float *>(&mv[p]);
+      float *vp = reinterpret_cast<float *>(&vv[p]);
+      if (e >= q.lo && e + 4 <= q.hi) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) adam_elem(wp[j], gp[j], mp[j], vp[j], c);
+        *reinterpret_cast<float4 *>(w + e) = wv[p];
+        *reinterpret_cast<float4 *>(m + e) = mv[p];
+        *reinterpret_cast<float4 *>(v + e) = vv[p];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (e + j >= q.lo && e + j < q.hi) {
+            adam_elem(wp[j], gp[j], mp[j], vp[j], c);
+            w[e + j] = wp[j];
+            m[e + j] = mp[j];
+            v[e + j] = vp[j];
+          }
+        }
+      }
+    }
+    // block amax over 8 lanes (an integer max of |x| bits also ranks NaN > Inf)
+    const uint32_t b0 = fbits(wv[p].x), b1 = fbits(wv[p].y), b2 = fbits(wv[p].z), b3 = fbits(wv[p].w);
+    uint32_t a = max(max(b0 & 0x7FFFFFFFu, b1 & 0x7FFFFFFFu), max(b2 & 0x7FFFFFFFu, b3 & 0x7FFFFFFFu));
+    a = max(a, (uint32_t)__shfl_xor((int)a, 1));
+    a = max(a, (uint32_t)__shfl_xor((int)a, 2));
+    a = max(a, (uint32_t)__shfl_xor((int)a, 4));
+    if (!live[p]) continue;
+    const uint32_t sb = mx_scale_byte(a);
+    uint32_t packed;
+    if (sb == 0xFFu) {
+      packed = 0x7F7F7F7Fu;
+    } else {
+      const int ex = (int)sb - 127;
+      packed = mx_e4m3_code(b0, ex) | (mx_e4m3_code(b1, ex) << 8) | (mx_e4m3_code(b2, ex) << 16) |
+               (mx_e4m3_code(b3, ex) << 24);
+    }
+    *reinterpret_cast<uint32_t *>(codes + e) = packed;
+    if ((t & 7) == 0) {
+      int64_t idx = e >> 5;
+      if (tile_layout) {
+        const QRegion r = regions[q.region];
+        const int64_t rel = e - r.abs;
+        const int64_t n = rel / r.cols;
+        const int64_t kb = (rel - n * r.cols) >> 5;
+        const int64_t KB = r.cols >> 5;
+        idx = (r.abs >> 5) + ((n >> 5) * (KB >> 2) + (kb >> 2)) * 128 + (n & 31) * 4 + (kb & 3);
+      }
+      scales[idx] = (uint8_t)sb;
+    }
+  }
+}
+
+AdamConst adam_const(const sshdp_adamw_hp &hp, int64_t step) {
+  AdamConst c;
+  c.lr = hp.lr;
+  c.b1 = hp.beta1;
+  c.b2 = hp.beta2;
+  c.eps = hp.eps;
+  c.decay = (float)(1.0 - (double)hp.lr * (double)hp.weight_decay);
+  c.omb1 = (float)(1.0 - (double)hp.beta1);
+  c.omb2 = (float)(1.0 - (double)hp.beta2);
+  c.bc1 = (float)(1.0 - std::pow((double)hp.beta1, (double)step));
+  c.bc2 = (float)(1.0 - std::pow((double)hp.beta2, (double)step));
+  return c;
+}
+
+}  // namespace
+
+hipError_t launch_f0(const sshdp_plan &p, const float *g, float *m, float mu, int nesterov, char *ws,
+                     hipStream_t s) {
+  if (p.f0tiles.empty()) return hipSuccess;
+  hipLaunchKernelGGL(k_f0, dim3((unsigned)p.f0tiles.size()), dim3(256), 0, s, p.d.munits, p.d.f0tiles, g, m, mu,
+                     nesterov, ws, reinterpret_cast<float *>(ws + p.ws_partials));
+  return hipGetLastError();
+}
+
+hipError_t launch_norm(const sshdp_plan &p, char *ws, float eps, hipStream_t s) {
+  if (p.munits.empty()) return hipSuccess;
+  hipLaunchKernelGGL(k_norm, dim3((unsigned)p.munits.size()), dim3(256), 0, s, p.d.munits,
+                     reinterpret_cast<const float *>(ws + p.ws_partials), reinterpret_cast<float *>(ws + p.ws_uscale),
+                     eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_adamw(const ASeg *segs, int64_t nseg, const sshdp_buffers &b, const sshdp_adamw_hp &hp,
+                        int64_t step, hipStream_t s) {
+  if (nseg <= 0) return hipSuccess;
+  const AdamConst c = adam_const(hp, step);
+  for (int64_t first = 0; first < nseg; first += 0x7FFFFFFF) {
+    const int64_t cnt = std::min<int64_t>(nseg - first, 0x7FFFFFFF);
+    hipLaunchKernelGGL(k_adamw, dim3((unsigned)cnt), dim3(256), 0, s, segs + first, b.w_main, b.grad, b.mom,
+                       b.adam_v, c);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant(const sshdp_plan &p, int64_t first, int64_t count, bool fused, const sshdp_buffers &b,
+                        const sshdp_adamw_hp *hp, int64_t step, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  const AdamConst c = fused ? adam_const(*hp, step) : AdamConst{};
+  const int tile = p.opts.scale_layout == SSHDP_SCALE_TILE32X4;
+  if (fused)
+    hipLaunchKernelGGL(k_quant<true>, dim3((unsigned)count), dim3(256), 0, s, p.d.qchunks + first, p.d.qregions, tile,
+                       b.w_main, b.grad, b.mom, b.adam_v, b.codes, b.scales, c);
+  else
+    hipLaunchKernelGGL(k_quant<false>, dim3((unsigned)count), dim3(256), 0, s, p.d.qchunks + first, p.d.qregions,
+                       tile, b.w_main, nullptr, nullptr, nullptr, b.codes, b.scales, c);
+  return hipGetLastError();
+}
+
+}  // namespace sshdp

@@ -1,0 +1,405 @@
+// plan.cpp -- host planner: resolves the data tree, validates it, groups the
+// update units and lays out the kernels' work tables.
+//
+// [SS-HSDP §3.2 "Data Tree"]: a child node is a view at an offset inside its
+// parent; only the root owns storage and children reach it through their
+// accumulated offset ("finalisation resolves child offsets", Appendix A).
+// [SS-HSDP §3.3]: compatible parameters are grouped so their updates batch;
+// [SS-HSDP §4.1]: the Newton-Schulz stage groups matrices with matching shapes
+// and layouts into batched GEMMs.  [SS-HSDP Appendix A, Table 4]: planning
+// rejects incompatible metadata, invalid geometry and storage overlap.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <new>
+#include <utility>
+
+#include "internal.h"
+
+using namespace sshdp;
+
+namespace {
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct Interval {
+  int64_t start, len;
+  int32_t opt;    // SSHDP_OPT_* of the owning unit
+  int32_t node;
+};
+
+// Row runs of a 2-D view: one interval if contiguous, else one per row.
+void view_intervals(int64_t abs, int64_t rows, int64_t cols, int64_t rs, int32_t opt, int32_t node,
+                    std::vector<Interval> &out) {
+  if (rows == 1 || rs == cols) {
+    out.push_back({abs, rows * cols, opt, node});
+  } else {
+    for (int64_t i = 0; i < rows; ++i) out.push_back({abs + i * rs, cols, opt, node});
+  }
+}
+
+bool any_overlap(std::vector<Interval> v) {
+  std::sort(v.begin(), v.end(), [](const Interval &a, const Interval &b) { return a.start < b.start; });
+  for (size_t i = 1; i < v.size(); ++i)
+    if (v[i].start < v[i - 1].start + v[i - 1].len) return true;
+  return false;
+}
+
+int validate(const sshdp_node *nodes, int32_t n, int64_t root_numel, int layout, std::vector<int64_t> &abs,
+             std::vector<int64_t> &ext) {
+  abs.assign(n, 0);
+  ext.assign(n, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    const sshdp_node &nd = nodes[i];
+    if (nd.parent < -1 || nd.parent >= i) return SSHDP_ERR_TREE;
+    const int64_t rs = nd.rows > 1 ? nd.row_stride : nd.cols;
+    if (nd.rows < 1 || nd.cols < 1 || nd.offset < 0 || rs < nd.cols) return SSHDP_ERR_SCHEMA;
+    const int64_t base = nd.parent < 0 ? 0 : abs[nd.parent];
+    const int64_t pext = nd.parent < 0 ? root_numel : ext[nd.parent];
+    const int64_t e = (nd.rows - 1) * rs + nd.cols;
+    const int64_t a = base + nd.offset;
+    if (nd.offset + e > pext || a + e > root_numel) return SSHDP_ERR_BOUNDS;
+    if (nd.is_unit && nd.optimizer != SSHDP_OPT_MUON && nd.optimizer != SSHDP_OPT_ADAMW)
+      return SSHDP_ERR_SCHEMA;
+    if (nd.is_unit && nd.optimizer == SSHDP_OPT_MUON) {
+      if (nd.rows < 2 || nd.cols < 2) return SSHDP_ERR_SCHEMA;
+      if (a % 4 || rs % 4 || nd.cols % 4) return SSHDP_ERR_SCHEMA;
+      if (nd.rows > (1 << 30) || nd.cols > (1 << 30)) return SSHDP_ERR_SCHEMA;
+    }
+    if (nd.quantize) {
+      if (rs != nd.cols || nd.cols % 32 || a % 32) return SSHDP_ERR_SCHEMA;
+      if (layout == SSHDP_SCALE_TILE32X4 && (nd.rows % 32 || nd.cols % 128)) return SSHDP_ERR_SCHEMA;
+      if (nd.cols > (1 << 30)) return SSHDP_ERR_SCHEMA;
+    }
+    abs[i] = a;
+    ext[i] = e;
+  }
+  std::vector<Interval> units, quant;
+  for (int32_t i = 0; i < n; ++i) {
+    const sshdp_node &nd = nodes[i];
+    const int64_t rs = nd.rows > 1 ? nd.row_stride : nd.cols;
+    if (nd.is_unit) view_intervals(abs[i], nd.rows, nd.cols, rs, nd.optimizer, i, units);
+  }
+  if (any_overlap(units)) return SSHDP_ERR_OVERLAP;
+  for (int32_t i = 0; i < n; ++i)
+    if (nodes[i].quantize) quant.push_back({abs[i], nodes[i].rows * nodes[i].cols, 0, i});
+  if (any_overlap(quant)) return SSHDP_ERR_OVERLAP;
+  return SSHDP_OK;
+}
+
+float scale_factor(int mode, int64_t rows, int64_t cols) {
+  if (mode == 1) return (float)std::sqrt(std::max(1.0, (double)rows / (double)cols));
+  if (mode == 2) return (float)(0.2 * std::sqrt((double)std::max(rows, cols)));
+  return 1.0f;
+}
+
+// GEMM macro-tile edge for a group's oriented shape.
+int pick_tile(int64_t r, int64_t c) {
+  (void)c;
+  return r >= 512 ? 256 : 128;
+}
+
+void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
+  std::map<std::pair<int64_t, int64_t>, std::vector<int32_t>> by_shape;  // ordered: deterministic
+  for (int32_t i = 0; i < n; ++i) {
+    if (!nodes[i].is_unit || nodes[i].optimizer != SSHDP_OPT_MUON) continue;
+    const int64_t r = std::min(nodes[i].rows, nodes[i].cols), c = std::max(nodes[i].rows, nodes[i].cols);
+    by_shape[{r, c}].push_back(i);
+  }
+  p.node_group.assign(n, -1);
+  size_t off = 0;
+  const int64_t n_muon = [&] {
+    int64_t k = 0;
+    for (auto &kv : by_shape) k += (int64_t)kv.second.size();
+    return k;
+  }();
+  p.ws_uscale = off;
+  off = round_up(off + n_muon * sizeof(float), kAlign);
+  // f0 tiles first (they size the partials buffer)
+  for (auto &kv : by_shape) {
+    Group g{};
+    g.r = (int32_t)kv.first.first;
+    g.c = (int32_t)kv.first.second;
+    g.tile = pick_tile(g.r, g.c);
+    g.r_pad = (int32_t)round_up(g.r, g.tile);
+    g.c_pad = (int32_t)round_up(g.c, g.tile);
+    g.n = (int32_t)kv.second.size();
+    g.unit_base = (int32_t)p.munits.size();
+    const int gi = (int)p.groups.size();
+    for (int32_t k = 0; k < g.n; ++k) {
+      const int32_t ni = kv.second[k];
+      const sshdp_node &nd = nodes[ni];
+      MuonUnit u{};
+      u.abs = p.node_abs[ni];
+      u.row_stride = nd.rows > 1 ? nd.row_stride : nd.cols;
+      u.rows = (int32_t)nd.rows;
+      u.cols = (int32_t)nd.cols;
+      u.tall = nd.rows > nd.cols ? 1 : 0;
+      u.group = gi;
+      u.idx = k;
+      u.upd_scale = scale_factor(p.opts.muon_scale_mode, nd.rows, nd.cols);
+      const int64_t Rp = u.tall ? g.c_pad : g.r_pad, Cp = u.tall ? g.r_pad : g.c_pad;
+      u.Rp = (int32_t)Rp;
+      u.Cp = (int32_t)Cp;
+      u.tile_begin = (int32_t)p.f0tiles.size();
+      for (int64_t tr = 0; tr < Rp / kF0Tile; ++tr)
+        for (int64_t tc = 0; tc < Cp / kF0Tile; ++tc)
+          p.f0tiles.push_back({(int32_t)p.munits.size(), (int32_t)tr, (int32_t)tc});
+      u.tile_end = (int32_t)p.f0tiles.size();
+      p.node_group[ni] = gi;
+      p.munits.push_back(u);
+      p.stats.muon_elems += nd.rows * nd.cols;
+      p.stats.ns_flops += (double)p.opts.ns_steps *
+                          (4.0 * (double)g.r * g.r * g.c + 2.0 * (double)g.r * g.r * g.r);
+    }
+    p.groups.push_back(g);
+  }
+  p.ws_partials = off;
+  off = round_up(off + p.f0tiles.size() * sizeof(float), kAlign);
+  for (Group &g : p.groups) {
+    const size_t xs = (size_t)g.n * g.r_pad * g.c_pad * 2, as = (size_t)g.n * g.r_pad * g.r_pad * 2;
+    g.off_x = off;   off = round_up(off + xs, kAlign);
+    g.off_xt0 = off; off = round_up(off + xs, kAlign);
+    g.off_xt1 = off; off = round_up(off + xs, kAlign);
+    g.off_a = off;   off = round_up(off + as, kAlign);
+    g.off_b = off;   off = round_up(off + as, kAlign);
+    for (int32_t k = 0; k < g.n; ++k) {
+      MuonUnit &u = p.munits[g.unit_base + k];
+      const int64_t ux = (int64_t)g.off_x + (int64_t)k * g.r_pad * g.c_pad * 2;
+      const int64_t ut = (int64_t)g.off_xt0 + (int64_t)k * g.r_pad * g.c_pad * 2;
+      u.ws_orig = u.tall ? ut : ux;     // a tall unit's own layout is X^T
+      u.ws_trans = u.tall ? ux : ut;
+    }
+  }
+  p.ws_bytes = off;
+  p.stats.n_muon_units = (int32_t)p.munits.size();
+  p.stats.n_groups = (int32_t)p.groups.size();
+}
+
+void build_elementwise(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
+  std::vector<Interval> units;
+  for (int32_t i = 0; i < n; ++i) {
+    const sshdp_node &nd = nodes[i];
+    if (!nd.is_unit) continue;
+    view_intervals(p.node_abs[i], nd.rows, nd.cols, nd.rows > 1 ? nd.row_stride : nd.cols, nd.optimizer, i,
+                   units);
+    if (nd.optimizer == SSHDP_OPT_ADAMW) {
+      p.stats.n_adamw_units++;
+      p.stats.adamw_elems += nd.rows * nd.cols;
+    }
+  }
+  std::sort(units.begin(), units.end(), [](const Interval &a, const Interval &b) { return a.start < b.start; });
+  std::vector<char> fused_node(n, 0);  // AdamW unit handled inside a fused region
+  std::vector<QChunk> fused, plain;
+  for (int32_t i = 0; i < n; ++i) {
+    const sshdp_node &nd = nodes[i];
+    if (!nd.quantize) continue;
+    const int32_t ri = (int32_t)p.qregions.size();
+    const int64_t a = p.node_abs[i], len = nd.rows * nd.cols;
+    p.qregions.push_back({a, nd.rows, (int32_t)nd.cols, 0});
+    p.stats.quant_elems += len;
+    // unit intervals intersecting the region
+    auto it = std::lower_bound(units.begin(), units.end(), a,
+                               [](const Interval &u, int64_t x) { return u.start + u.len <= x; });
+    std::vector<Interval> inside;
+    bool eligible = true;
+    for (; it != units.end() && it->start < a + len; ++it) {
+      if (it->start + it->len <= a) continue;
+      inside.push_back(*it);
+      if (it->opt != SSHDP_OPT_ADAMW) eligible = false;
+      if (it->start < a || it->start + it->len > a + len) eligible = false;
+    }
+    // every AdamW unit touching the region must lie entirely inside it
+    if (eligible) {
+      for (const Interval &iv : inside) {
+        const sshdp_node &un = nodes[iv.node];
+        const int64_t rs = un.rows > 1 ? un.row_stride : un.cols;
+        const int64_t ua = p.node_abs[iv.node], ue = ua + (un.rows - 1) * rs + un.cols;
+        if (ua < a || ue > a + len) eligible = false;
+      }
+      for (size_t k = 1; k < inside.size() && eligible; ++k)   // no two runs share a block
+        if ((inside[k].start / 32) <= ((inside[k - 1].start + inside[k - 1].len - 1) / 32)) eligible = false;
+    }
+    std::vector<QChunk> &dst = eligible ? fused : plain;
+    size_t next = 0;
+    int64_t pos = a;
+    while (pos < a + len) {
+      int64_t end = std::min(a + len, pos + (int64_t)kChunk);
+      if (eligible) {
+        // a new chunk starts at the block of every run start, so a chunk holds at most one run
+        while (next < inside.size() && inside[next].start / 32 * 32 <= pos) ++next;
+        if (next < inside.size()) {
+          const int64_t rb = inside[next].start / 32 * 32;
+          if (rb > pos && rb < end) end = rb;
+        }
+      }
+      QChunk q{};
+      q.base = pos;
+      q.n = (int32_t)(end - pos);
+      q.region = ri;
+      q.lo = q.hi = pos;
+      if (eligible) {
+        for (const Interval &iv : inside) {
+          const int64_t lo = std::max(iv.start, pos), hi = std::min(iv.start + iv.len, end);
+          if (lo < hi) { q.lo = lo; q.hi = hi; break; }
+        }
+      }
+      dst.push_back(q);
+      pos = end;
+    }
+    if (eligible) {
+      for (const Interval &iv : inside) fused_node[iv.node] = 1;
+      p.stats.fused_quant_elems += len;
+    }
+  }
+  p.n_qchunks_fused = (int64_t)fused.size();
+  p.qchunks = fused;
+  p.qchunks.insert(p.qchunks.end(), plain.begin(), plain.end());
+  p.stats.n_quant_regions = (int32_t)p.qregions.size();
+  for (const Interval &iv : units) {
+    if (iv.opt != SSHDP_OPT_ADAMW) continue;
+    for (int64_t s = iv.start; s < iv.start + iv.len; s += kChunk) {
+      ASeg sg{s, (int32_t)std::min<int64_t>(kChunk, iv.start + iv.len - s), 0};
+      p.aseg_all.push_back(sg);
+      if (!fused_node[iv.node]) p.aseg_unfused.push_back(sg);
+    }
+  }
+}
+
+template <class T>
+size_t table_bytes(const std::vector<T> &v) { return round_up((int64_t)(v.size() * sizeof(T)), 256); }
+
+int upload(sshdp_plan &p) {
+  const size_t total = table_bytes(p.munits) + table_bytes(p.f0tiles) + table_bytes(p.aseg_all) +
+                       table_bytes(p.aseg_unfused) + table_bytes(p.qregions) + table_bytes(p.qchunks) + 256;
+  if (hipGetDevice(&p.device) != hipSuccess) return SSHDP_ERR_HIP;
+  if (hipMalloc(&p.dblock, total) != hipSuccess) { p.dblock = nullptr; return SSHDP_ERR_HIP; }
+  std::vector<char> host(total, 0);
+  size_t off = 0;
+  auto put = [&](auto &vec, auto *&dptr) {
+    using T = typename std::remove_reference<decltype(vec)>::type::value_type;
+    if (!vec.empty()) std::memcpy(host.data() + off, vec.data(), vec.size() * sizeof(T));
+    dptr = reinterpret_cast<T *>(static_cast<char *>(p.dblock) + off);
+    off += table_bytes(vec);
+  };
+  put(p.munits, p.d.munits);
+  put(p.f0tiles, p.d.f0tiles);
+  put(p.aseg_all, p.d.aseg_all);
+  put(p.aseg_unfused, p.d.aseg_unfused);
+  put(p.qregions, p.d.qregions);
+  put(p.qchunks, p.d.qchunks);
+  if (hipMemcpy(p.dblock, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) return SSHDP_ERR_HIP;
+  return SSHDP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sshdp_abi_version(void) { return SSHDP_ABI_VERSION; }
+
+const char *sshdp_status_string(int code) {
+  switch (code) {
+    case SSHDP_OK: return "ok";
+    case SSHDP_ERR_ARG: return "invalid argument";
+    case SSHDP_ERR_TREE: return "data tree: parent is not an earlier node";
+    case SSHDP_ERR_BOUNDS: return "view leaves its parent or the root";
+    case SSHDP_ERR_OVERLAP: return "units or quantised regions share storage";
+    case SSHDP_ERR_SCHEMA: return "geometry or metadata the kernels cannot take";
+    case SSHDP_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case SSHDP_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSHDP_ERR_HIP: return "HIP runtime error";
+    case SSHDP_ERR_STATE: return "plan is host-only";
+    default: return "unknown status";
+  }
+}
+
+int sshdp_default_opts(sshdp_plan_opts *o) {
+  if (!o) return SSHDP_ERR_ARG;
+  o->ns_steps = 5;
+  o->ns_a = 3.4445f;
+  o->ns_b = -4.7750f;
+  o->ns_c = 2.0315f;
+  o->ns_eps = 1e-7f;
+  o->scale_layout = SSHDP_SCALE_ROWMAJOR;
+  o->nesterov = 0;
+  o->muon_scale_mode = 0;
+  o->flags = 0;
+  return SSHDP_OK;
+}
+
+int sshdp_plan_views(const sshdp_node *nodes, int32_t n_nodes, int64_t root_numel, const sshdp_plan_opts *opts,
+                     sshdp_plan **out_plan) {
+  if (!out_plan) return SSHDP_ERR_ARG;
+  *out_plan = nullptr;
+  if (!nodes || n_nodes <= 0 || root_numel <= 0) return SSHDP_ERR_ARG;
+  sshdp_plan_opts o;
+  if (opts) o = *opts; else sshdp_default_opts(&o);
+  if (o.ns_steps < 1 || o.ns_steps > 64 || (o.scale_layout != SSHDP_SCALE_ROWMAJOR &&
+      o.scale_layout != SSHDP_SCALE_TILE32X4) || o.muon_scale_mode < 0 || o.muon_scale_mode > 2 ||
+      !(o.ns_eps >= 0.0f) || (o.flags & ~1u))
+    return SSHDP_ERR_ARG;
+  std::vector<int64_t> abs, ext;
+  int st = validate(nodes, n_nodes, root_numel, o.scale_layout, abs, ext);
+  if (st != SSHDP_OK) return st;
+  sshdp_plan *p = new (std::nothrow) sshdp_plan();
+  if (!p) return SSHDP_ERR_ARG;
+  p->root_numel = root_numel;
+  p->opts = o;
+  p->node_abs = abs;
+  p->stats.root_numel = root_numel;
+  p->stats.scale_bytes = (root_numel + 31) / 32;
+  p->stats.n_nodes = n_nodes;
+  for (int32_t i = 0; i < n_nodes; ++i) p->stats.n_units += nodes[i].is_unit ? 1 : 0;
+  build_muon(*p, nodes, n_nodes);
+  build_elementwise(*p, nodes, n_nodes);
+  p->stats.workspace_bytes = (int64_t)p->ws_bytes;
+  p->host_only = (o.flags & SSHDP_PLAN_HOST_ONLY) != 0;
+  if (!p->host_only) {
+    st = upload(*p);
+    if (st != SSHDP_OK) {
+      sshdp_plan_destroy(p);
+      return st;
+    }
+  }
+  *out_plan = p;
+  return SSHDP_OK;
+}
+
+int sshdp_plan_info(const sshdp_plan *p, sshdp_plan_stats *s) {
+  if (!p || !s) return SSHDP_ERR_ARG;
+  *s = p->stats;
+  return SSHDP_OK;
+}
+
+int sshdp_plan_group(const sshdp_plan *p, int32_t g, sshdp_group_info *info) {
+  if (!p || !info || g < 0 || g >= (int32_t)p->groups.size()) return SSHDP_ERR_ARG;
+  const Group &G = p->groups[g];
+  info->r = G.r; info->c = G.c; info->r_pad = G.r_pad; info->c_pad = G.c_pad;
+  info->n_units = G.n; info->tile = G.tile;
+  return SSHDP_OK;
+}
+
+int sshdp_plan_node(const sshdp_plan *p, int32_t node, int64_t *abs_offset, int32_t *group) {
+  if (!p || node < 0 || node >= (int32_t)p->node_abs.size()) return SSHDP_ERR_ARG;
+  if (abs_offset) *abs_offset = p->node_abs[node];
+  if (group) *group = p->node_group[node];
+  return SSHDP_OK;
+}
+
+void sshdp_plan_destroy(sshdp_plan *p) {
+  if (!p) return;
+  if (p->dblock) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (p->device >= 0 && cur != p->device) (void)hipSetDevice(p->device);
+    (void)hipFree(p->dblock);
+    if (cur >= 0 && cur != p->device) (void)hipSetDevice(cur);
+  }
+  for (auto &e : p->prof_pending) { (void)hipEventDestroy(e.second.first); (void)hipEventDestroy(e.second.second); }
+  for (hipEvent_t e : p->prof_pool) (void)hipEventDestroy(e);
+  delete p;
+}
+
+}  // extern "C"

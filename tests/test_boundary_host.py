@@ -1,0 +1,140 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every function
+include/sshdp.h declares, and its planner (run host-only) resolves offsets,
+rejects bad trees with the same error class as the oracle's rule list
+[SS-HSDP Appendix A, Table 4], and groups Muon units by oriented shape
+[SS-HSDP §4.1].  No compute call is made."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mxfp8_weight_repack_amd as sh
+from mxfp8_weight_repack_amd import _lib
+import oracle
+from oracle.views import ViewError
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "sshdp.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(sshdp_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    decl = _declared()
+    assert len(decl) >= 14
+    L = sh.lib()
+    for name in decl:
+        assert hasattr(L, name), name
+        assert name in _lib.SIGNATURES, name
+    assert set(_lib.SIGNATURES) == set(decl)
+    assert L.sshdp_abi_version() == 1
+    assert L.sshdp_status_string(-5) == b"geometry or metadata the kernels cannot take"
+
+
+def _plan(nodes, n, layout="rowmajor"):
+    return sh.Plan(nodes, n, layout=layout, host_only=True)
+
+
+def _random_tree(rng, N):
+    nodes = []
+    for i in range(int(rng.integers(1, 7))):
+        p = int(rng.integers(-1, i)) if i else -1
+        if rng.uniform() < 0.05:
+            p = int(rng.integers(-3, i + 2))
+        rows = int(rng.integers(0 if rng.uniform() < 0.03 else 1, 6))
+        cols = int(rng.choice([4, 8, 12, 32, 64, 96, 128, 5, 37]))
+        rs = cols + int(rng.choice([0, 0, 0, 4, 32, -2]))
+        off = int(rng.choice([0, 4, 8, 32, 64, 3, 128, 256]))
+        unit = rng.uniform() < 0.6
+        opt = rng.choice(["muon", "adamw"]) if unit else None
+        if unit and rng.uniform() < 0.03:
+            opt = "sgd"
+        q = rng.uniform() < 0.3
+        nodes.append(dict(parent=p, offset=off, rows=rows, cols=cols, row_stride=rs, is_unit=unit,
+                          optimizer=opt, quantize=q))
+    return nodes
+
+
+@pytest.mark.parametrize("layout", ["rowmajor", "tile32x4"])
+def test_planner_agrees_with_oracle_rules_on_random_trees(layout):
+    rng = np.random.default_rng(42 if layout == "rowmajor" else 43)
+    n_ok = n_err = 0
+    for _ in range(3000):
+        nodes = _random_tree(rng, 2048)
+        try:
+            res = oracle.resolve_views(nodes, 2048, layout)
+            exp = None
+        except ViewError as e:
+            exp = e.code
+        try:
+            p = _plan(nodes, 2048, layout)
+            got = None
+        except sh.SshdpError as e:
+            got = e.name
+        assert got == exp, (nodes, got, exp)
+        if exp is None:
+            n_ok += 1
+            for i, r in enumerate(res):
+                assert p.node(i)[0] == r["abs"]
+            st = p.stats()
+            assert st["muon_elems"] == sum(r["rows"] * r["cols"] for r in res if r["optimizer"] == "muon")
+            assert st["adamw_elems"] == sum(r["rows"] * r["cols"] for r in res if r["optimizer"] == "adamw")
+            assert st["quant_elems"] == sum(r["rows"] * r["cols"] for r in res if r["quantize"])
+        else:
+            n_err += 1
+    assert n_ok > 100 and n_err > 100
+
+
+def test_planner_groups_and_stats_on_workloads():
+    for cid in (1, 2, 3, 4, 5):
+        wl = workloads.config(cid)
+        p = _plan(wl.nodes, wl.root_numel, wl.scale_layout)
+        st = p.stats()
+        assert st["muon_elems"] + st["adamw_elems"] == wl.params
+        assert st["scale_bytes"] == (wl.root_numel + 31) // 32
+        shapes = {}
+        for i, n in enumerate(wl.nodes):
+            if n["is_unit"] and n["optimizer"] == "muon":
+                key = (min(n["rows"], n["cols"]), max(n["rows"], n["cols"]))
+                shapes[key] = shapes.get(key, 0) + 1
+        got = {(g["r"], g["c"]): g["n_units"] for g in p.groups()}
+        assert got == shapes
+        flops = sum(cnt * 5 * (4 * r * r * c + 2 * r ** 3) for (r, c), cnt in shapes.items())
+        assert abs(st["ns_flops"] - flops) <= 1e-9 * max(flops, 1)
+        for g in p.groups():
+            assert g["r_pad"] % g["tile"] == 0 and g["c_pad"] % g["tile"] == 0
+            assert g["r_pad"] - g["r"] < g["tile"] and g["c_pad"] - g["c"] < g["tile"]
+    # the flat shard's requant is fused with AdamW everywhere; the dense block's is not
+    wl = workloads.config(4, small=True)
+    st = _plan(wl.nodes, wl.root_numel).stats()
+    assert st["fused_quant_elems"] == st["quant_elems"] == wl.root_numel
+    wl = workloads.config(2, small=True)
+    st = _plan(wl.nodes, wl.root_numel, "tile32x4").stats()
+    assert st["fused_quant_elems"] == 0
+
+
+def test_planner_argument_errors():
+    wl = workloads.config(1)
+    with pytest.raises(sh.SshdpError) as e:
+        sh.Plan(wl.nodes, wl.root_numel, ns_steps=0, host_only=True)
+    assert e.value.name == "ARG"
+    with pytest.raises(sh.SshdpError) as e:
+        sh.Plan([], 10, host_only=True)
+    assert e.value.name == "ARG"
+    p = _plan(wl.nodes, wl.root_numel, "tile32x4")
+    # a host-only plan refuses to launch, before touching any pointer
+    b = sh.buffers(8, 16, 32, 48, 64, 80)
+    with pytest.raises(sh.SshdpError) as e:
+        sh.update_step(p, b, sh.muon_hp(), sh.adamw_hp(), 1, 0, 0)
+    assert e.value.name == "STATE"
+    with pytest.raises(sh.SshdpError) as e:
+        sh.requant_mxfp8(p, 16, 32, 48)
+    assert e.value.name == "STATE"
+    p.destroy()
+    p.destroy()

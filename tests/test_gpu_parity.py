@@ -1,0 +1,293 @@
+"""GPU parity: the HIP library (through its C ABI) against the oracle on the
+same seeded inputs.
+
+Gates (stated per test):
+* MXFP8 codes and scales: bit-exact when both sides quantise the same fp32
+  weight (the GPU-updated weight is fed to the oracle's quantiser);
+* AdamW main weights: normwise relative error <= 1e-6
+  (max |w_gpu - w_ref| / max |w_ref|);
+* Newton-Schulz: per unit, relative Frobenius error <= 2e-2 of the direction
+  recovered from the weight change, v = (w_before - w_after) / lr;
+* zero-gradient units: bit-identical weights; elements outside every unit:
+  untouched.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.views import resolve_views, unit_indices
+import mxfp8_weight_repack_amd as sh
+import workloads
+from gpu_util import DeviceState, oracle_step, rel_fro, say, MUON, ADAM
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+NS_TOL = 2e-2
+ADAM_TOL = 1e-6
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sh.lib()
+
+
+def _bf16_host(x):
+    return oracle.bf16_rne(x).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------- GEMM
+@pytest.mark.parametrize("tile,M,N,K,batch", [(128, 128, 256, 192, 2), (128, 384, 128, 640, 3),
+                                              (256, 256, 512, 320, 2), (256, 512, 256, 128, 1)])
+def test_gemm_nt_against_fp64(tile, M, N, K, batch):
+    say(f"gemm tile={tile} M={M} N={N} K={K} batch={batch}")
+    r = np.random.default_rng(M * 7 + N + K + tile)
+    P = r.standard_normal((batch, M, K)).astype(np.float32)
+    Q = r.standard_normal((batch, N, K)).astype(np.float32)
+    D = r.standard_normal((batch, M, N)).astype(np.float32)
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).cuda()
+    tP, tQ, tD = bf(P), bf(Q), bf(D)
+    O = torch.zeros(batch, M, N, dtype=torch.bfloat16, device="cuda")
+    OT = torch.zeros(batch, N, M, dtype=torch.bfloat16, device="cuda")
+    sh.gemm_bf16_nt(tP, tQ, tD, O, OT, M, N, K, batch, 0.75, -1.5, tile,
+                    torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref = 0.75 * np.einsum("bik,bjk->bij", _bf16_host(P), _bf16_host(Q)) - 1.5 * _bf16_host(D)
+    got = O.float().cpu().numpy().astype(np.float64)
+    scale = np.sqrt(K) + 2.0
+    assert np.max(np.abs(got - ref)) <= 2 ** -7 * scale * 1.5 + 1e-3
+    assert rel_fro(got, ref) < 4e-3
+    assert torch.equal(OT, O.transpose(1, 2).contiguous())
+
+
+# ----------------------------------------------------------------------------- G alone
+def _specials(w, wl):
+    """Plant NaN/Inf/-0/subnormal/zero blocks inside the quantised regions."""
+    w = w.copy()
+    res = resolve_views(wl.nodes, wl.root_numel)
+    q = [r for r in res if r["quantize"]]
+    a = q[0]["abs"]
+    w[a:a + 32] = 0.0
+    w[a + 32:a + 64] = -0.0
+    w[a + 64 + 5] = np.nan
+    w[a + 96 + 31] = np.inf
+    w[a + 128:a + 160] = np.float32(1e-41)
+    w[a + 160] = np.float32(448.0)
+    w[a + 192:a + 224] *= np.float32(1e30)
+    return w
+
+
+@pytest.mark.parametrize("case", ["c1", "c2s", "c3s", "c4s", "c5s", "ragged"])
+@pytest.mark.parametrize("layout", ["rowmajor", "tile32x4"])
+def test_requant_bit_exact(case, layout):
+    wl = workloads.ragged_mix() if case == "ragged" else workloads.config(int(case[1]), small=case.endswith("s"))
+    if layout == "tile32x4" and wl.scale_layout != "tile32x4":
+        pytest.skip("workload has quantised regions that are not 32x128 tiles")
+    say(f"requant {wl.name} {layout}")
+    w0, _ = wl.arrays()
+    w = _specials(w0, wl)
+    st = DeviceState(wl, w=w, layout=layout)
+    st.codes.fill_(0xAB)
+    st.scales.fill_(0xCD)
+    sh.requant_mxfp8(st.plan, st.w, st.codes, st.scales, st.stream())
+    h = st.host()
+    codes = np.full(wl.root_numel, 0xAB, np.uint8)
+    scales = np.full(st.stats["scale_bytes"], 0xCD, np.uint8)
+    res = resolve_views(wl.nodes, wl.root_numel, layout)
+    oracle.requant_root(w, res, layout, codes, scales)
+    assert np.array_equal(h["codes"], codes)
+    assert np.array_equal(h["scales"], scales)
+    assert np.array_equal(h["w"].view(np.uint32), w.view(np.uint32))
+
+
+# ----------------------------------------------------------------------------- AdamW alone
+def test_adamw_alone_matches_oracle_over_steps():
+    wl = workloads.config(4, small=True)
+    say(f"adamw {wl.name}")
+    w0, g = wl.arrays()
+    st = DeviceState(wl)
+    w, m, v = w0.copy(), np.zeros_like(w0), np.zeros_like(w0)
+    res = resolve_views(wl.nodes, wl.root_numel)
+    for t in (1, 2, 3):
+        sh.update_adamw(st.plan, st.bufs(), sh.adamw_hp(**ADAM), t, st.stream())
+        for r in res:
+            if r["is_unit"]:
+                idx = unit_indices(r)
+                w[idx], m[idx], v[idx] = oracle.adamw_step(w[idx], g[idx], m[idx], v[idx], t, **ADAM)
+        h = st.host()
+        assert np.max(np.abs(h["w"] - w)) <= ADAM_TOL * np.max(np.abs(w))
+        assert np.max(np.abs(h["m"] - m)) <= 1e-6 * np.max(np.abs(m))
+        assert np.max(np.abs(h["v"] - v)) <= 1e-5 * np.max(np.abs(v))
+    pad = np.ones(wl.root_numel, bool)
+    for r in res:
+        if r["is_unit"]:
+            pad[unit_indices(r).ravel()] = False
+    assert np.all(h["w"][pad] == 0) and np.all(h["m"][pad] == 0) and np.all(h["v"][pad] == 0)
+
+
+# ----------------------------------------------------------------------------- whole step
+CASES = ["c1", "c2s", "c3s", "c4s", "c5s", "ragged"]
+
+
+def _wl(case):
+    return workloads.ragged_mix() if case == "ragged" else workloads.config(int(case[1]),
+                                                                            small=case.endswith("s"))
+
+
+def check_step(wl, layout, h, ref, dirs, w0, muon_lr=MUON["lr"], units=None):
+    res = resolve_views(wl.nodes, wl.root_numel, layout)
+    touched = np.zeros(wl.root_numel, bool)
+    worst = 0.0
+    for i, r in enumerate(res):
+        if not r["is_unit"]:
+            continue
+        idx = unit_indices(r)
+        touched[idx.ravel()] = True
+        if units is not None and i not in units:
+            continue
+        if r["optimizer"] == "muon":
+            if i in wl.zero_grad_units:
+                assert np.array_equal(h["w"][idx].view(np.uint32), w0[idx].view(np.uint32)), i
+                continue
+            v_gpu = (w0[idx].astype(np.float64) - h["w"][idx].astype(np.float64)) / np.float32(muon_lr)
+            e = rel_fro(v_gpu, dirs[i])
+            worst = max(worst, e)
+            assert e <= NS_TOL, (i, r["rows"], r["cols"], e)
+            assert np.max(np.abs(h["m"][idx] - ref["m"][idx])) <= 1e-6 * max(np.max(np.abs(ref["m"][idx])), 1e-30)
+        else:
+            ww, wr = h["w"][idx], ref["w"][idx]
+            assert np.max(np.abs(ww - wr)) <= ADAM_TOL * np.max(np.abs(wr)), i
+    if units is None:
+        assert np.array_equal(h["w"][~touched].view(np.uint32), w0[~touched].view(np.uint32))
+        assert np.all(h["m"][~touched] == 0) and np.all(h["v"][~touched] == 0)
+    # G on the GPU-updated weight: bit-exact against the oracle's quantiser
+    codes = np.zeros(wl.root_numel, np.uint8)
+    scales = np.zeros((wl.root_numel + 31) // 32, np.uint8)
+    oracle.requant_root(h["w"], res, layout, codes, scales)
+    qmask = np.zeros(wl.root_numel, bool)
+    for r in res:
+        if r["quantize"]:
+            qmask[unit_indices(r).ravel()] = True
+    assert np.array_equal(h["codes"][qmask], codes[qmask])
+    smask = np.zeros(scales.size, bool)
+    smask[np.nonzero(qmask)[0] // 32] = True
+    assert np.array_equal(h["scales"][smask], scales[smask])
+    return worst
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_update_step_parity(case):
+    wl = _wl(case)
+    say(f"update_step {wl.name} ({wl.scale_layout})")
+    w0, g = wl.arrays()
+    st = DeviceState(wl)
+    st.step(1)
+    h = st.host()
+    z = np.zeros_like(w0)
+    ref, dirs = oracle_step(wl, wl.scale_layout, w0, g, z, z, 1)
+    worst = check_step(wl, wl.scale_layout, h, ref, dirs, w0)
+    say(f"  worst NS rel-Frobenius {worst:.3e}")
+
+
+def test_update_step_equals_separate_calls_bitwise():
+    wl = workloads.config(4, small=True)
+    for w_l in (wl, workloads.ragged_mix(), workloads.config(2, small=True)):
+        say(f"fused vs separate {w_l.name}")
+        a = DeviceState(w_l)
+        b = DeviceState(w_l)
+        a.step(1)
+        sh.update_muon(b.plan, b.bufs(), sh.muon_hp(**MUON), b.ws, b.ws_bytes, b.stream())
+        sh.update_adamw(b.plan, b.bufs(), sh.adamw_hp(**ADAM), 1, b.stream())
+        sh.requant_mxfp8(b.plan, b.w, b.codes, b.scales, b.stream())
+        ha, hb = a.host(), b.host()
+        for k in ha:
+            assert np.array_equal(ha[k].view(np.uint8), hb[k].view(np.uint8)), k
+
+
+def test_determinism_and_resume():
+    """Two runs are bitwise equal; N steps == k steps, state copied out and
+    reloaded into fresh buffers, then N-k steps (the caller owns all state)."""
+    wl = workloads.config(2, small=True)
+    say(f"determinism/resume {wl.name}")
+    a = DeviceState(wl)
+    for t in (1, 2, 3, 4):
+        a.step(t)
+    ha = a.host()
+    b = DeviceState(wl)
+    for t in (1, 2):
+        b.step(t)
+    hb = b.host()
+    c = DeviceState(wl, w=hb["w"], m=hb["m"], v=hb["v"])
+    for t in (3, 4):
+        c.step(t)
+    hc = c.host()
+    for k in ("w", "m", "v", "codes"):
+        assert np.array_equal(ha[k].view(np.uint8), hc[k].view(np.uint8)), k
+    d = DeviceState(wl)
+    for t in (1, 2, 3, 4):
+        d.step(t)
+    hd = d.host()
+    for k in ha:
+        assert np.array_equal(ha[k].view(np.uint8), hd[k].view(np.uint8)), k
+
+
+def test_multi_step_against_oracle():
+    """Three steps: momentum and AdamW state evolve on both sides."""
+    wl = workloads.config(1)
+    say(f"3 steps {wl.name}")
+    w0, g = wl.arrays()
+    st = DeviceState(wl)
+    w, m, v = w0.copy(), np.zeros_like(w0), np.zeros_like(w0)
+    for t in (1, 2, 3):
+        st.step(t)
+        h = st.host()
+        ref, dirs = oracle_step(wl, wl.scale_layout, w, g, m, v, t)
+        # compare against the oracle started from the GPU's own previous state
+        check_step(wl, wl.scale_layout, h, ref, dirs, w)
+        w, m, v = h["w"].copy(), h["m"].copy(), h["v"].copy()
+
+
+def test_options_nesterov_scale_mode_weight_decay():
+    wl = workloads.ragged_mix()
+    say(f"options {wl.name}")
+    w0, g = wl.arrays()
+    st = DeviceState(wl, plan_kw=dict(nesterov=True, scale_mode=1))
+    muon = dict(lr=0.02, momentum=0.9, weight_decay=0.05)
+    m0 = (np.random.default_rng(5).standard_normal(w0.size) * 1e-3).astype(np.float32)
+    st.m.copy_(torch.from_numpy(m0))
+    st.step(1, muon=muon)
+    h = st.host()
+    hp = oracle.OracleHyper(lr=0.02, momentum=0.9, weight_decay=0.05, nesterov=True, scale_mode=1)
+    res = resolve_views(wl.nodes, wl.root_numel)
+    for i, r in enumerate(res):
+        if not (r["is_unit"] and r["optimizer"] == "muon"):
+            continue
+        idx = unit_indices(r)
+        w_ref, m_ref, vdir = oracle.muon_update_unit(w0[idx], g[idx], m0[idx], hp)
+        s = oracle.muon_scale(1, r["rows"], r["cols"])
+        decay = np.float32(1 - np.float64(np.float32(0.02)) * np.float64(np.float32(0.05)))
+        v_gpu = (w0[idx].astype(np.float64) * decay - h["w"][idx]) / (np.float32(0.02) * s)
+        assert rel_fro(v_gpu, vdir) <= NS_TOL, i
+        assert np.max(np.abs(h["m"][idx] - m_ref)) <= 1e-6 * np.max(np.abs(m_ref))
+
+
+def test_argument_errors_on_device():
+    wl = workloads.config(1)
+    st = DeviceState(wl)
+    with pytest.raises(sh.SshdpError) as e:
+        sh.update_step(st.plan, st.bufs(), sh.muon_hp(), sh.adamw_hp(), 0, st.ws, st.ws_bytes, st.stream())
+    assert e.value.name == "ARG"
+    with pytest.raises(sh.SshdpError) as e:
+        sh.update_muon(st.plan, st.bufs(), sh.muon_hp(), st.ws, st.ws_bytes - 256, st.stream())
+    assert e.value.name == "WORKSPACE"
+    b = sh.buffers(st.w.data_ptr() + 4, st.g, st.m, st.v, st.codes, st.scales)
+    with pytest.raises(sh.SshdpError) as e:
+        sh.update_step(st.plan, b, sh.muon_hp(), sh.adamw_hp(), 1, st.ws, st.ws_bytes, st.stream())
+    assert e.value.name == "ALIGN"
+    # nothing was launched: state unchanged
+    h = st.host()
+    w0, _ = wl.arrays()
+    assert np.array_equal(h["w"], w0) and np.all(h["m"] == 0)
