@@ -1,0 +1,186 @@
+"""Benchmark: one MI355X's share of the SS-HSDP update phase.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu]
+
+A step is one sshdp_update_step over the whole workload: Muon momentum,
+batched bf16 MFMA Newton-Schulz, main-weight update, AdamW, and the MXFP8
+requantisation of every runtime weight.  Inputs are seeded synthetic roots,
+resident in HBM before timing starts.  The default workload is the dense
+transformer block (d=2048, 16 heads of 128, 4 KV heads, MLP 8192, per-head
+QKV Muon units), the configuration the metric is quoted on.
+
+Prints one JSON line.  `value` = parameters updated per second (padding
+excluded) from hipEvents around K steps on the launch stream.  `roofline`
+describes the dominant kernel (the Newton-Schulz MFMA contraction): its
+algorithmic flops per launch divided by its average launch duration, from
+HIP events bracketing every launch in a second pass of K steps.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
+METRIC = "update-step params/sec (Muon+AdamW+MXFP8 repack); NS MFMA %, repack HBM %"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=25.0, help="seconds of oracle work to aim for")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, budget_s):
+    """Time the oracle (as it stands) on a bounded sample of the workload's
+    units: units are taken in table order until the estimated cost fills the
+    budget; params/s = sampled params / oracle time."""
+    import oracle
+    from oracle.views import resolve_views, unit_indices
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    w0, g = wl.arrays()
+    res = resolve_views(wl.nodes, wl.root_numel, wl.scale_layout)
+    # cost model for picking the sample: ~0.3 us/element elementwise, ~25 GF/s per BLAS thread for NS
+    pick, est = [], 0.0
+    for i, r in enumerate(res):
+        if not r["is_unit"]:
+            continue
+        n = r["rows"] * r["cols"]
+        cost = 3e-7 * n
+        if r["optimizer"] == "muon":
+            rr, cc = min(r["rows"], r["cols"]), max(r["rows"], r["cols"])
+            cost += 5 * (4 * rr * rr * cc + 2 * rr ** 3) / (25e9 * threads)
+        if est + cost > budget_s and pick:
+            continue
+        pick.append(i)
+        est += cost
+    sub = [dict(wl.nodes[i], parent=-1, offset=res[i]["abs"]) for i in pick]
+    w, m, v = w0.copy(), np.zeros_like(w0), np.zeros_like(w0)
+    codes = np.zeros(wl.root_numel, np.uint8)
+    scales = np.zeros((wl.root_numel + 31) // 32, np.uint8)
+    # quantise the sampled units' own elements (their share of G)
+    for nd in sub:
+        nd["quantize"] = nd["cols"] % 32 == 0 and nd["row_stride"] == nd["cols"] and nd["offset"] % 32 == 0
+    params = sum(nd["rows"] * nd["cols"] for nd in sub)
+    t0 = time.perf_counter()
+    oracle.update_step(sub, wl.root_numel, w, g, m, v, codes, scales, 1, layout="rowmajor")
+    dt = time.perf_counter() - t0
+    return {"value": params / dt, "unit": "params/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(sub)} of {len(wl.units())} units ({params} params, one full update step "
+                      f"incl. their MXFP8 repack) in {dt:.1f} s; NumPy/OpenBLAS fp64, {threads} BLAS threads",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+              f"multi-GPU path: run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import mxfp8_weight_repack_amd as sh
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    wl = workloads.config(args.config)
+    w0, g0 = wl.arrays()
+    plan = sh.Plan(wl.nodes, wl.root_numel, layout=wl.scale_layout)
+    st = plan.stats()
+    w = torch.from_numpy(w0).to(dev)
+    g = torch.from_numpy(g0).to(dev)
+    m = torch.zeros_like(w)
+    v = torch.zeros_like(w) if st["n_adamw_units"] else None
+    codes = torch.zeros(wl.root_numel, dtype=torch.uint8, device=dev)
+    scales = torch.zeros(st["scale_bytes"], dtype=torch.uint8, device=dev)
+    ws_bytes = max(int(st["workspace_bytes"]), 256)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    bufs = sh.buffers(w, g, m, v, codes, scales)
+    mhp, ahp = sh.muon_hp(), sh.adamw_hp()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    step = 0
+    for _ in range(args.warmup):
+        step += 1
+        sh.update_step(plan, bufs, mhp, ahp, step, ws, ws_bytes, sp)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step += 1
+        sh.update_step(plan, bufs, mhp, ahp, step, ws, ws_bytes, sp)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    value = wl.params / (ms / 1e3)
+
+    # per-kernel-class durations: HIP events bracketing every launch, same K steps
+    plan.profile(True)
+    for _ in range(args.steps):
+        step += 1
+        sh.update_step(plan, bufs, mhp, ahp, step, ws, ws_bytes, sp)
+    torch.cuda.synchronize()
+    prof = plan.profile_read()
+    plan.profile(False)
+    ns_ms = sum(prof[c][0] for c in ("ns_gram", "ns_poly", "ns_update"))
+    ns_launches = sum(prof[c][1] for c in ("ns_gram", "ns_poly", "ns_update"))
+    components = {c: {"ms_per_step": prof[c][0] / args.steps, "launches_per_step": prof[c][1] / args.steps}
+                  for c in prof if prof[c][1]}
+    roofline = None
+    if ns_launches:
+        flops_per_launch = st["ns_flops"] * args.steps / ns_launches
+        avg_launch_s = ns_ms / ns_launches / 1e3
+        achieved = flops_per_launch / avg_launch_s / 1e12
+        roofline = {"bound": "mfma", "kernel": "k_gemm_nt (all Newton-Schulz contraction launches)",
+                    "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                    "flops_per_launch": flops_per_launch, "avg_launch_us": avg_launch_s * 1e6}
+    # repack (G) HBM fraction: algorithmic bytes 4 (read w) + 1 (code) + 1/32 (scale) per element,
+    # plus 28 B/element of AdamW where it is fused
+    rq_ms = prof["requant"][0] + prof["adamw_requant"][0]
+    repack = None
+    if rq_ms > 0:
+        fused = st["fused_quant_elems"]
+        byts = (st["quant_elems"] - fused) * 5.03125 + fused * 29.03125
+        gbs = byts * args.steps / (rq_ms / 1e3) / 1e9
+        repack = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": gbs / HBM_PEAK_GBS, "bytes_per_step": byts}
+    out = {
+        "metric": METRIC, "value": value, "unit": "params/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "params": wl.params, "root_numel": wl.root_numel,
+                   "muon_units": st["n_muon_units"], "adamw_units": st["n_adamw_units"],
+                   "ns_groups": [[gi["r"], gi["c"], gi["n_units"]] for gi in plan.groups()],
+                   "scale_layout": wl.scale_layout, "ns_tflop_per_step": st["ns_flops"] / 1e12},
+        "roofline": roofline, "repack_roofline": repack, "components": components,
+    }
+    if not args.no_cpu:
+        cb = cpu_baseline(wl, args.cpu_budget)
+        cb.pop("seconds", None)
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
