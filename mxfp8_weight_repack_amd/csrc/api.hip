@@ -37,11 +37,11 @@ struct Prof {
     if (!p->prof) return;
     e0 = take();
     e1 = take();
-    if (e0) hipEventRecord(e0, s);
+    if (e0) (void)hipEventRecord(e0, s);
   }
   ~Prof() {
     if (!p->prof || !e0 || !e1) return;
-    hipEventRecord(e1, s);
+    (void)hipEventRecord(e1, s);
     p->prof_pending.push_back({cls, {e0, e1}});
   }
   hipEvent_t take() {

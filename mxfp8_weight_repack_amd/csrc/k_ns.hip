@@ -53,21 +53,48 @@ struct GemmArgs {
 __device__ __forceinline__ float bf16_to_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 __device__ __forceinline__ uint16_t f_to_bf16(float x) { return (uint16_t)mx_bf16_bits(__float_as_uint(x)); }
 
+// One BK = 64 slice of the macro tile from LDS: 4 K-steps of 16, each
+// MB A fragments and MB B fragments (16 bytes per lane) and MB*MB MFMAs.
+template <int MB, int PITCH, int OPS>
+__device__ __forceinline__ void mma_step(const uint16_t *__restrict__ s, int fa, int fb, f32x16_t (&acc)[MB][MB]) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    bf16x8_t af[MB], bfr[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) af[i] = *reinterpret_cast<const bf16x8_t *>(&s[fa + i * 32 * PITCH + kk * 16]);
+#pragma unroll
+    for (int j = 0; j < MB; ++j)
+      bfr[j] = *reinterpret_cast<const bf16x8_t *>(&s[OPS + fb + j * 32 * PITCH + kk * 16]);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < MB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  }
+}
+
 template <int TILE, bool FINAL>
 __global__ __launch_bounds__(256, 1) void k_gemm_nt(GemmArgs a) {
-  constexpr int BK = 64, PITCH = BK + 8;
-  constexpr int WT = TILE / 2, MB = WT / 32;
-  constexpr int LPT = TILE * BK / 8 / 256;          // 16-byte loads per thread per operand
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][TILE * PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][TILE * PITCH];
+  constexpr int BK = 64, PITCH = BK + 8;             // LDS row: 64 bf16 + 16 bytes of padding
+  constexpr int WT = TILE / 2, MB = WT / 32;         // wave tile, 32x32 blocks per wave edge
+  constexpr int LPT = TILE * BK / 8 / 256;           // 16-byte loads per thread per operand
+  constexpr int OPS = TILE * PITCH;                  // one operand tile in LDS (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * OPS];   // [buf][A|B]
 
   const int b = blockIdx.y;
   const int tiles_n = a.N / TILE;
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
-  const uint16_t *P = a.P + b * a.sP + (int64_t)tm * TILE * a.K;
-  const uint16_t *Q = a.Q + b * a.sQ + (int64_t)tn * TILE * a.K;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  const int64_t K = a.K;
+
+  // global -> LDS copy: thread t moves rows (t>>3) + 32 i, 16 bytes at column (t&7)*8
+  const uint16_t *gA = a.P + b * a.sP + ((int64_t)tm * TILE + (t >> 3)) * K + (t & 7) * 8;
+  const uint16_t *gB = a.Q + b * a.sQ + ((int64_t)tn * TILE + (t >> 3)) * K + (t & 7) * 8;
+  const int sofs = (t >> 3) * PITCH + (t & 7) * 8;
+  // fragment reads: lane holds row (lane&31) of a 32-row block, 8 K-values at (lane>>5)*8
+  const int fa = (wm * WT + (lane & 31)) * PITCH + (lane >> 5) * 8;
+  const int fb = (wn * WT + (lane & 31)) * PITCH + (lane >> 5) * 8;
 
   f32x16_t acc[MB][MB];
 #pragma unroll
@@ -78,52 +105,38 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nt(GemmArgs a) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   uint4 ra[LPT], rb[LPT];
-  auto gload = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int ch = t + 256 * i, row = ch >> 3, c8 = ch & 7;
-      ra[i] = *reinterpret_cast<const uint4 *>(P + (int64_t)row * a.K + k0 + c8 * 8);
-      rb[i] = *reinterpret_cast<const uint4 *>(Q + (int64_t)row * a.K + k0 + c8 * 8);
-    }
-  };
-  auto sstore = [&](int buf) {
+  for (int i = 0; i < LPT; ++i) {
+    ra[i] = *reinterpret_cast<const uint4 *>(gA + (int64_t)i * 32 * K);
+    rb[i] = *reinterpret_cast<const uint4 *>(gB + (int64_t)i * 32 * K);
+  }
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int ch = t + 256 * i, row = ch >> 3, c8 = ch & 7;
-      *reinterpret_cast<uint4 *>(&sA[buf][row * PITCH + c8 * 8]) = ra[i];
-      *reinterpret_cast<uint4 *>(&sB[buf][row * PITCH + c8 * 8]) = rb[i];
-    }
-  };
-  auto compute = [&](int buf) {
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t af[MB], bfr[MB];
-      const int kof = kk * 16 + (lane >> 5) * 8;
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t *>(&sA[buf][(wm * WT + i * 32 + (lane & 31)) * PITCH + kof]);
-#pragma unroll
-      for (int j = 0; j < MB; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t *>(&sB[buf][(wn * WT + j * 32 + (lane & 31)) * PITCH + kof]);
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < MB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-  };
+  for (int i = 0; i < LPT; ++i) {
+    *reinterpret_cast<uint4 *>(&smem[sofs + i * 32 * PITCH]) = ra[i];
+    *reinterpret_cast<uint4 *>(&smem[OPS + sofs + i * 32 * PITCH]) = rb[i];
+  }
+  __syncthreads();
 
   const int nk = a.K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    compute(cur);
-    if (kt + 1 < nk) sstore(cur ^ 1);
+  int cur = 0;
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const int64_t k0 = (int64_t)(kt + 1) * BK;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      ra[i] = *reinterpret_cast<const uint4 *>(gA + (int64_t)i * 32 * K + k0);
+      rb[i] = *reinterpret_cast<const uint4 *>(gB + (int64_t)i * 32 * K + k0);
+    }
+    mma_step<MB, PITCH, OPS>(smem + cur, fa, fb, acc);
+    const int nxt = 2 * OPS - cur;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      *reinterpret_cast<uint4 *>(&smem[nxt + sofs + i * 32 * PITCH]) = ra[i];
+      *reinterpret_cast<uint4 *>(&smem[nxt + OPS + sofs + i * 32 * PITCH]) = rb[i];
+    }
     __syncthreads();
+    cur = nxt;
   }
+  mma_step<MB, PITCH, OPS>(smem + cur, fa, fb, acc);
 
   // ---- epilogue: element (m, n) of a 32x32 block sits in lane n + 32*((m/4)%2),
   // register (m/8)*4 + m%4; each lane holds 4 consecutive rows of one column.
