@@ -158,7 +158,10 @@ typedef struct {
   int32_t n_nodes, n_units, n_muon_units, n_adamw_units, n_quant_regions, n_groups;
   int64_t muon_elems, adamw_elems, quant_elems;
   int64_t fused_quant_elems;  /* quantised elements G handles inside the AdamW pass       */
-  double ns_flops;            /* 5*(4 r^2 c + 2 r^3)-style dense count over all Muon units */
+  double ns_flops;            /* steps*(4 r^2 c + 2 r^3) summed over Muon units: the dense count */
+  double ns_tile_flops;       /* MFMA flops the tile schedule executes per step (symmetric Gram and
+                                 poly computed as tm <= tn tiles; padding to the tile included; units
+                                 whose momentum is all zero skip theirs at run time)             */
 } sshdp_plan_stats;
 
 /* One Newton-Schulz batch: the Muon units sharing an oriented shape r x c
@@ -220,9 +223,10 @@ int sshdp_update_step(const sshdp_plan *plan, const sshdp_buffers *bufs, const s
 
 /* Diagnostics.  The batched NT contraction used by Newton-Schulz, exposed to
  * test it alone: for b < batch, O[b] = bf16(alpha * P[b] Q[b]^T + beta * D[b])
- * with P[b] M x K, Q[b] N x K, D[b], O[b] M x N (bf16, row-major, dense, batch
- * strides M*K, N*K, M*N); OT (optional) receives O[b]^T (N x M).  M, N must be
- * multiples of `tile` (64, 128 or 256), K of 64; D may be NULL (beta ignored). */
+ * with P[b] M x K, Q[b] N x K, O[b] M x N (bf16, row-major, dense, batch strides
+ * M*K, N*K, M*N).  D is passed TRANSPOSED, DT[b] N x M (the layout in which the
+ * update product reads X), or NULL (beta ignored); OT (optional) receives
+ * O[b]^T (N x M).  M, N must be multiples of `tile` (128 or 256), K of 64. */
 int sshdp_gemm_bf16_nt(const void *P, const void *Q, const void *D, void *O, void *OT, int32_t M,
                        int32_t N, int32_t K, int32_t batch, float alpha, float beta, int32_t tile,
                        void *stream);

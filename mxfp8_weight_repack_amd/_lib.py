@@ -64,7 +64,8 @@ class PlanStats(ctypes.Structure):
                 ("n_muon_units", ctypes.c_int32), ("n_adamw_units", ctypes.c_int32),
                 ("n_quant_regions", ctypes.c_int32), ("n_groups", ctypes.c_int32),
                 ("muon_elems", ctypes.c_int64), ("adamw_elems", ctypes.c_int64), ("quant_elems", ctypes.c_int64),
-                ("fused_quant_elems", ctypes.c_int64), ("ns_flops", ctypes.c_double)]
+                ("fused_quant_elems", ctypes.c_int64), ("ns_flops", ctypes.c_double),
+                ("ns_tile_flops", ctypes.c_double)]
 
 
 class GroupInfo(ctypes.Structure):

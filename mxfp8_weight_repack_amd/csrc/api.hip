@@ -77,23 +77,21 @@ int run_muon(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_muon_hp *h
   if (e != hipSuccess) return SSHDP_ERR_HIP;
   const int steps = p->opts.ns_steps;
   for (int it = 0; it < steps; ++it) {
-    for (const Group &g : p->groups) {
-      {
-        Prof pr(p, 2, s);
-        e = launch_ns_stage(*p, g, 0, it, w, b->w_main, hp->lr, hp->weight_decay, s);
-      }
-      if (e != hipSuccess) return SSHDP_ERR_HIP;
-      {
-        Prof pr(p, 3, s);
-        e = launch_ns_stage(*p, g, 1, it, w, b->w_main, hp->lr, hp->weight_decay, s);
-      }
-      if (e != hipSuccess) return SSHDP_ERR_HIP;
-      {
-        Prof pr(p, 4, s);
-        e = launch_ns_stage(*p, g, it + 1 == steps ? 3 : 2, it, w, b->w_main, hp->lr, hp->weight_decay, s);
-      }
-      if (e != hipSuccess) return SSHDP_ERR_HIP;
+    {
+      Prof pr(p, 2, s);
+      e = launch_ns_stage(*p, 0, it, w, b->w_main, hp->lr, hp->weight_decay, s);
     }
+    if (e != hipSuccess) return SSHDP_ERR_HIP;
+    {
+      Prof pr(p, 3, s);
+      e = launch_ns_stage(*p, 1, it, w, b->w_main, hp->lr, hp->weight_decay, s);
+    }
+    if (e != hipSuccess) return SSHDP_ERR_HIP;
+    {
+      Prof pr(p, 4, s);
+      e = launch_ns_stage(*p, it + 1 == steps ? 3 : 2, it, w, b->w_main, hp->lr, hp->weight_decay, s);
+    }
+    if (e != hipSuccess) return SSHDP_ERR_HIP;
   }
   return SSHDP_OK;
 }

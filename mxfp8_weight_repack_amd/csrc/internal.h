@@ -12,6 +12,7 @@
 namespace sshdp {
 
 constexpr int kF0Tile = 64;          // f0 transposing tile edge (elements)
+constexpr int kNsTile = 128;         // Newton-Schulz GEMM macro-tile edge (elements)
 constexpr int kChunk = 4096;         // elements per AdamW / requant work item
 constexpr size_t kAlign = 256;       // workspace sub-buffer alignment (bytes)
 
@@ -45,6 +46,17 @@ struct Group {
   size_t off_x, off_xt0, off_xt1, off_a, off_b;   // workspace byte offsets
 };
 
+// Newton-Schulz group as the kernels see it.
+struct NsGroupDev {
+  int64_t off_x, off_xt0, off_xt1, off_a, off_b;   // workspace byte offsets
+  int32_t r_pad, c_pad, unit_base, n;
+};
+
+// One macro tile of one stage: group, unit within the group, tile row/column.
+struct NsTile {
+  int32_t group, b, tm, tn;
+};
+
 // AdamW work item: a contiguous run of unit elements (<= kChunk).
 struct ASeg {
   int64_t base;
@@ -76,6 +88,10 @@ struct DeviceTables {
   ASeg *aseg_unfused = nullptr;
   QRegion *qregions = nullptr;
   QChunk *qchunks = nullptr;
+  NsGroupDev *ns_groups = nullptr;
+  NsTile *ns_gram = nullptr;
+  NsTile *ns_poly = nullptr;
+  NsTile *ns_update = nullptr;
 };
 
 }  // namespace sshdp
@@ -88,6 +104,8 @@ struct sshdp_plan {
   std::vector<sshdp::MuonUnit> munits;
   std::vector<sshdp::F0Tile> f0tiles;
   std::vector<sshdp::Group> groups;
+  std::vector<sshdp::NsGroupDev> ns_groups;
+  std::vector<sshdp::NsTile> ns_gram, ns_poly, ns_update;   // per-stage tile tables, longest K first
   std::vector<sshdp::ASeg> aseg_all, aseg_unfused;
   std::vector<sshdp::QRegion> qregions;
   std::vector<sshdp::QChunk> qchunks;   // fused-eligible chunks first
@@ -111,9 +129,9 @@ namespace sshdp {
 hipError_t launch_f0(const sshdp_plan &p, const float *g, float *m, float mu, int nesterov, char *ws,
                      hipStream_t s);
 hipError_t launch_norm(const sshdp_plan &p, char *ws, float eps, hipStream_t s);
-// stage: 0 Gram, 1 poly, 2 update, 3 final update (+f2)
-hipError_t launch_ns_stage(const sshdp_plan &p, const Group &g, int stage, int iter, char *ws,
-                           float *w_main, float lr, float wd, hipStream_t s);
+// stage: 0 Gram, 1 poly, 2 update, 3 final update (+f2); one launch covers all groups
+hipError_t launch_ns_stage(const sshdp_plan &p, int stage, int iter, char *ws, float *w_main, float lr, float wd,
+                           hipStream_t s);
 hipError_t launch_gemm_raw(const void *P, const void *Q, const void *D, void *O, void *OT, int M, int N,
                            int K, int batch, float alpha, float beta, int tile, hipStream_t s);
 hipError_t launch_adamw(const ASeg *segs, int64_t nseg, const sshdp_buffers &b, const sshdp_adamw_hp &hp,

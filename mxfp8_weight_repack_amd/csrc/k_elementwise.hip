@@ -109,7 +109,8 @@ __global__ __launch_bounds__(256) void k_norm(const MuonUnit *__restrict__ units
   __syncthreads();
   if (threadIdx.x == 0) {
     const float tot = (red[0] + red[1]) + (red[2] + red[3]);
-    uscale[blockIdx.x] = 1.0f / (sqrtf(tot) + eps);
+    // an all-zero unit gets scale 0: its Newton-Schulz products are skipped (direction exactly 0)
+    uscale[blockIdx.x] = tot > 0.f ? 1.0f / (sqrtf(tot) + eps) : 0.f;
   }
 }
 

@@ -9,22 +9,30 @@
 // stated setting:
 //     A = X X^T;  B = b A + c A A;  X <- a X + B X.
 //
-// Every product here is one batched "NT" contraction O = alpha P Q^T + beta D
-// with both operands K-contiguous, which is the layout the MFMA operands want:
+// Every product is one "NT" contraction O = alpha P Q^T + beta D with both
+// operands K-contiguous, the layout the MFMA operands want:
 //   Gram    A = X X^T            P = Q = X   (r x c)
 //   poly    B = c A A + b A      P = Q = A   (A symmetric, so A A^T = A A)
 //   update  X' = a X + B X       P = B, Q = X^T (c x r), D = X; the epilogue
-//           writes X' and X'^T, the operands of the next step, so no
-//           separate transpose pass exists.
-// The normalisation is folded into the first step's scalars: with s =
-// 1/(||u|| + eps), A0 = s^2 u u^T and X1 = s (B0 u) + a s u, so u is never
-// rescaled in memory.  A tall unit is iterated on its transpose (same map:
-// X (X^T X) = (X X^T) X); its own layout simply plays the role of X^T.
+//           writes X' and X'^T, the operands of the next step (no transpose pass)
+// A and B are symmetric: only tiles with tm <= tn are computed and each
+// off-diagonal tile is also stored mirrored.  The normalisation is folded into
+// the first step's scalars: with s = 1/(||u|| + eps), A0 = s^2 u u^T and
+// X1 = s (B0 u) + a s u.  A unit whose momentum is all zero has s = 0 and skips
+// every product (its direction is exactly zero).  A tall unit is iterated on
+// its transpose (same map: X (X^T X) = (X X^T) X); its own layout plays the
+// role of X^T.
 //
-// Kernel: a TILE x TILE macro tile per workgroup of 4 waves (2 x 2), each wave
+// One launch per stage covers every group and unit (a tile table built by the
+// planner, longest-K tiles first), so small per-head units and large matrices
+// share the machine instead of running one underfilled launch each.
+//
+// Tile kernel: TILE x TILE per workgroup of 4 waves (2 x 2), each wave
 // (TILE/2)^2 as (TILE/64)^2 blocks of v_mfma_f32_32x32x16_bf16; K in steps of
-// 64 through double-buffered LDS (rows padded by 16 bytes: conflict-free
-// 16-byte fragment reads); fp32 accumulation; epilogue in fp32.
+// 64; operands move global -> LDS with global_load_lds_dwordx4 (no VGPR
+// staging), double-buffered; 128-byte LDS rows whose 16-byte chunks are XOR-
+// swizzled so fragment reads are bank-conflict free; fragment reads for the
+// next 16-wide K slice are interleaved with the current slice's MFMAs.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -36,67 +44,46 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-struct GemmArgs {
-  const uint16_t *P, *Q, *D;
-  uint16_t *O, *OT;
-  int64_t sP, sQ, sD, sO, sOT;     // batch strides (elements)
-  int M, N, K;                     // P: M x K, Q: N x K, D/O: M x N, OT: N x M
-  float alpha, beta;
-  const float *uscale;             // per-unit 1/(||u|| + eps)
-  int alpha_pow, beta_pow;         // alpha *= s^alpha_pow, beta *= s^beta_pow
-  int unit_base;                   // batch b <-> unit unit_base + b
-  const MuonUnit *units;           // FINAL: the units' views into w
-  float *w;
-  float lr, decay;                 // FINAL: w <- w*decay - lr*scale*x
-};
+constexpr int BK = 64;             // K elements per LDS stage
 
-__device__ __forceinline__ float bf16_to_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-__device__ __forceinline__ uint16_t f_to_bf16(float x) { return (uint16_t)mx_bf16_bits(__float_as_uint(x)); }
-
-// One BK = 64 slice of the macro tile from LDS: 4 K-steps of 16, each
-// MB A fragments and MB B fragments (16 bytes per lane) and MB*MB MFMAs.
-template <int MB, int PITCH, int OPS>
-__device__ __forceinline__ void mma_step(const uint16_t *__restrict__ s, int fa, int fb, f32x16_t (&acc)[MB][MB]) {
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    bf16x8_t af[MB], bfr[MB];
-#pragma unroll
-    for (int i = 0; i < MB; ++i) af[i] = *reinterpret_cast<const bf16x8_t *>(&s[fa + i * 32 * PITCH + kk * 16]);
-#pragma unroll
-    for (int j = 0; j < MB; ++j)
-      bfr[j] = *reinterpret_cast<const bf16x8_t *>(&s[OPS + fb + j * 32 * PITCH + kk * 16]);
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int j = 0; j < MB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-  }
+// LDS bytes a TILE kernel needs: the double-buffered operand stages, or the
+// epilogue's padded bf16 tile, whichever is larger
+template <int TILE>
+constexpr int smem_bytes() {
+  return 4 * TILE * BK * 2 > TILE * (TILE + 8) * 2 ? 4 * TILE * BK * 2 : TILE * (TILE + 8) * 2;
 }
 
-template <int TILE, bool FINAL>
-__global__ __launch_bounds__(256, 1) void k_gemm_nt(GemmArgs a) {
-  constexpr int BK = 64, PITCH = BK + 8;             // LDS row: 64 bf16 + 16 bytes of padding
-  constexpr int WT = TILE / 2, MB = WT / 32;         // wave tile, 32x32 blocks per wave edge
-  constexpr int LPT = TILE * BK / 8 / 256;           // 16-byte loads per thread per operand
-  constexpr int OPS = TILE * PITCH;                  // one operand tile in LDS (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * OPS];   // [buf][A|B]
+__device__ __forceinline__ float bf16_to_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-  const int b = blockIdx.y;
-  const int tiles_n = a.N / TILE;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+// Physical 16-byte chunk = logical chunk ^ swz(row): any 8 consecutive rows
+// (and any 16) read at one logical chunk land on distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// C[TILE x TILE] = P[TILE x K] Q[TILE x K]^T, P and Q row-major with row pitch
+// K elements (bf16), starting at byte addresses gP, gQ (uniform).
+template <int TILE>
+__device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_t K, char *smem,
+                                          f32x16_t (&acc)[TILE / 64][TILE / 64]) {
+  constexpr int WT = TILE / 2, MB = WT / 32;
+  constexpr int SEG = TILE * BK * 2;                 // bytes of one operand tile
+  constexpr int NI = TILE / 32;                      // DMA instructions per thread per operand
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t K = a.K;
 
-  // global -> LDS copy: thread t moves rows (t>>3) + 32 i, 16 bytes at column (t&7)*8
-  const uint16_t *gA = a.P + b * a.sP + ((int64_t)tm * TILE + (t >> 3)) * K + (t & 7) * 8;
-  const uint16_t *gB = a.Q + b * a.sQ + ((int64_t)tn * TILE + (t >> 3)) * K + (t & 7) * 8;
-  const int sofs = (t >> 3) * PITCH + (t & 7) * 8;
-  // fragment reads: lane holds row (lane&31) of a 32-row block, 8 K-values at (lane>>5)*8
-  const int fa = (wm * WT + (lane & 31)) * PITCH + (lane >> 5) * 8;
-  const int fb = (wn * WT + (lane & 31)) * PITCH + (lane >> 5) * 8;
+  // DMA: instruction i of wave w fills rows 8*(4i + w) .. +7, 8 lanes per row;
+  // lane i of an instruction lands at LDS base + 16*i
+  const int drow = 8 * wave + (lane >> 3);
+  const int dchunk = (lane & 7) ^ swz(drow);         // rows drow + 32 i share the swizzle
+  const uint32_t loff = (uint32_t)(drow * K + dchunk * 8) * 2u;
+  const int dlds = wave * 1024;
 
-  f32x16_t acc[MB][MB];
+  // fragment reads: lane holds row (lane & 31) of a 32-row block, logical chunk 2 kk + (lane >> 5)
+  const int lrow = lane & 31;
+  const int ra = (wm * WT + lrow) * 128, rb = (wn * WT + lrow) * 128;
+  int cofs[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) cofs[kk] = ((2 * kk + (lane >> 5)) ^ swz(lrow)) * 16;
+
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -104,174 +91,291 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nt(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  uint4 ra[LPT], rb[LPT];
+  auto dma = [&](int stage, int64_t k0) __attribute__((always_inline)) {
+    char *sa = smem + stage * 2 * SEG;
 #pragma unroll
-  for (int i = 0; i < LPT; ++i) {
-    ra[i] = *reinterpret_cast<const uint4 *>(gA + (int64_t)i * 32 * K);
-    rb[i] = *reinterpret_cast<const uint4 *>(gB + (int64_t)i * 32 * K);
-  }
+    for (int i = 0; i < NI; ++i) {
+      const int64_t ob = ((int64_t)i * 32 * K + k0) * 2;
+      __builtin_amdgcn_global_load_lds(gP + ob + loff,
+                                       (__attribute__((address_space(3))) void *)(sa + dlds + i * 4096), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(gQ + ob + loff,
+                                       (__attribute__((address_space(3))) void *)(sa + SEG + dlds + i * 4096), 16, 0,
+                                       0);
+    }
+  };
+  bf16x8_t fa0[MB], fb0[MB], fa1[MB], fb1[MB];
+  auto ldfrag = [&](const char *sa, int kk, bf16x8_t(&fa_)[MB], bf16x8_t(&fb_)[MB]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < LPT; ++i) {
-    *reinterpret_cast<uint4 *>(&smem[sofs + i * 32 * PITCH]) = ra[i];
-    *reinterpret_cast<uint4 *>(&smem[OPS + sofs + i * 32 * PITCH]) = rb[i];
-  }
+    for (int i = 0; i < MB; ++i) fa_[i] = *reinterpret_cast<const bf16x8_t *>(sa + ra + i * 32 * 128 + cofs[kk]);
+#pragma unroll
+    for (int j = 0; j < MB; ++j)
+      fb_[j] = *reinterpret_cast<const bf16x8_t *>(sa + SEG + rb + j * 32 * 128 + cofs[kk]);
+  };
+  auto mma = [&](bf16x8_t(&fa_)[MB], bf16x8_t(&fb_)[MB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < MB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_[i], fb_[j], acc[i][j], 0, 0, 0);
+    // each MFMA followed by one fragment read of the next slice
+#pragma unroll
+    for (int i = 0; i < 2 * MB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if (MB * MB > 2 * MB) __builtin_amdgcn_sched_group_barrier(0x008, MB * MB - 2 * MB, 0);
+  };
+
+  const int nk = (int)(K / BK);
+  dma(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-
-  const int nk = a.K / BK;
-  int cur = 0;
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    const int64_t k0 = (int64_t)(kt + 1) * BK;
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      ra[i] = *reinterpret_cast<const uint4 *>(gA + (int64_t)i * 32 * K + k0);
-      rb[i] = *reinterpret_cast<const uint4 *>(gB + (int64_t)i * 32 * K + k0);
-    }
-    mma_step<MB, PITCH, OPS>(smem + cur, fa, fb, acc);
-    const int nxt = 2 * OPS - cur;
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      *reinterpret_cast<uint4 *>(&smem[nxt + sofs + i * 32 * PITCH]) = ra[i];
-      *reinterpret_cast<uint4 *>(&smem[nxt + OPS + sofs + i * 32 * PITCH]) = rb[i];
-    }
+  ldfrag(smem, 0, fa0, fb0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nk) dma(st ^ 1, (int64_t)(kt + 1) * BK);
+    const char *sa = smem + st * 2 * SEG;
+    ldfrag(sa, 1, fa1, fb1);
+    mma(fa0, fb0);
+    ldfrag(sa, 2, fa0, fb0);
+    mma(fa1, fb1);
+    ldfrag(sa, 3, fa1, fb1);
+    mma(fa0, fb0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    cur = nxt;
+    if (kt + 1 < nk) ldfrag(smem + (st ^ 1) * 2 * SEG, 0, fa0, fb0);
+    mma(fa1, fb1);
   }
-  mma_step<MB, PITCH, OPS>(smem + cur, fa, fb, acc);
+}
 
-  // ---- epilogue: element (m, n) of a 32x32 block sits in lane n + 32*((m/4)%2),
-  // register (m/8)*4 + m%4; each lane holds 4 consecutive rows of one column.
-  float alpha = a.alpha, beta = a.beta;
-  const int unit = a.unit_base + b;
-  if (a.alpha_pow | a.beta_pow) {
-    const float s = a.uscale[unit];
-    if (a.alpha_pow == 1) alpha *= s;
-    if (a.alpha_pow == 2) alpha *= s * s;
-    if (a.beta_pow == 1) beta *= s;
-  }
-  const uint16_t *D = a.D ? a.D + b * a.sD : nullptr;
-  uint16_t *O = a.O ? a.O + b * a.sO : nullptr;
-  uint16_t *OT = a.OT ? a.OT + b * a.sOT : nullptr;
-  MuonUnit u{};
-  int r_unit = 0, c_unit = 0;
-  if (FINAL) {
-    u = a.units[unit];
-    r_unit = u.tall ? u.cols : u.rows;
-    c_unit = u.tall ? u.rows : u.cols;
-  }
+// Epilogue of a TILE x TILE product: x = alpha*acc + beta*D, rounded to bf16,
+// stored row-major to O (leading dim ldo) and, if OT, transposed to OT[col*ldt + row].
+// D is read through its transpose DT (DT[col*lddt + row] = D[row][col]): element
+// (m, n) of a 32x32 MFMA block sits in lane n + 32*((m/4)%2), register
+// (m/8)*4 + m%4, so a lane holds 4 consecutive rows of one column and both the
+// D^T read and the O^T write are 8 contiguous bytes.  The row-major O store goes
+// through LDS (bf16 tile, padded rows) so each lane writes 16 contiguous bytes.
+// smem must be free (all fragment reads done) and hold TILE*(TILE+8)*2 bytes.
+template <int TILE>
+__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TILE / 64][TILE / 64], float alpha, float beta,
+                                           const uint16_t *DT, int64_t lddt, uint16_t *O, int64_t ldo, uint16_t *OT,
+                                           int64_t ldt, int r0, int c0, char *smem) {
+  constexpr int WT = TILE / 2, MB = WT / 32, LP = TILE + 8;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
+  uint16_t *lt = reinterpret_cast<uint16_t *>(smem);
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
-      const int col = tn * TILE + wn * WT + j * 32 + (lane & 31);
+      const int lc = wn * WT + j * 32 + (lane & 31);
+      const int col = c0 + lc;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int row0 = tm * TILE + wm * WT + i * 32 + g4 * 8 + (lane >> 5) * 4;
+        const int lr0 = wm * WT + i * 32 + g4 * 8 + (lane >> 5) * 4;
+        const int row0 = r0 + lr0;
         float x[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) x[q] = alpha * acc[i][j][g4 * 4 + q];
-        if (D) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) x[q] = fmaf(beta, bf16_to_f(D[(int64_t)(row0 + q) * a.N + col]), x[q]);
+        if (DT) {
+          const uint2 d = *reinterpret_cast<const uint2 *>(DT + (int64_t)col * lddt + row0);
+          x[0] = fmaf(beta, __uint_as_float(d.x << 16), x[0]);
+          x[1] = fmaf(beta, __uint_as_float(d.x & 0xFFFF0000u), x[1]);
+          x[2] = fmaf(beta, __uint_as_float(d.y << 16), x[2]);
+          x[3] = fmaf(beta, __uint_as_float(d.y & 0xFFFF0000u), x[3]);
         }
-        if (!FINAL) {
-          uint16_t h[4];
+        uint32_t h[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            h[q] = f_to_bf16(x[q]);
-            O[(int64_t)(row0 + q) * a.N + col] = h[q];
-          }
-          if (OT) {
-            uint2 pk;
-            pk.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-            pk.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-            *reinterpret_cast<uint2 *>(OT + (int64_t)col * a.M + row0) = pk;
-          }
-        } else if (col < c_unit) {
-          const float ls = a.lr * u.upd_scale;
+        for (int q = 0; q < 4; ++q) {
+          h[q] = mx_bf16_bits(__float_as_uint(x[q]));
+          lt[(lr0 + q) * LP + lc] = (uint16_t)h[q];
+        }
+        if (OT) {
+          uint2 pk;
+          pk.x = h[0] | (h[1] << 16);
+          pk.y = h[2] | (h[3] << 16);
+          *reinterpret_cast<uint2 *>(OT + (int64_t)col * ldt + row0) = pk;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int CH = TILE / 8;                       // 16-byte chunks per row
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int row = row0 + q;
-            if (row < r_unit) {
-              const int64_t idx = u.tall ? u.abs + (int64_t)col * u.row_stride + row
-                                         : u.abs + (int64_t)row * u.row_stride + col;
-              a.w[idx] = fmaf(a.w[idx], a.decay, -ls * x[q]);
-            }
+  for (int k = 0; k < TILE * CH / 256; ++k) {
+    const int id = t + 256 * k, row = id / CH, ch = id - row * CH;
+    const uint4 v = *reinterpret_cast<const uint4 *>(&lt[row * LP + ch * 8]);
+    *reinterpret_cast<uint4 *>(O + (int64_t)(r0 + row) * ldo + c0 + ch * 8) = v;
+  }
+}
+
+// f2 on a tile of the last update product: w <- w*decay - lr*scale*x for the
+// elements inside the unit (oriented r x c; a tall unit's view is the transpose).
+template <int TILE>
+__device__ __forceinline__ void final_tile(const f32x16_t (&acc)[TILE / 64][TILE / 64], float alpha, float beta,
+                                           const uint16_t *DT, int64_t lddt, const MuonUnit &u, float *w, float lr,
+                                           float decay, int r0, int c0, bool zero) {
+  constexpr int WT = TILE / 2, MB = WT / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+  const int r_unit = u.tall ? u.cols : u.rows, c_unit = u.tall ? u.rows : u.cols;
+  const float ls = lr * u.upd_scale;
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      const int col = c0 + wn * WT + j * 32 + (lane & 31);
+      if (col >= c_unit) continue;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int row0 = r0 + wm * WT + i * 32 + g4 * 8 + (lane >> 5) * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = row0 + q;
+          if (row >= r_unit) continue;
+          float x = 0.f;
+          if (!zero) {
+            x = alpha * acc[i][j][g4 * 4 + q];
+            x = fmaf(beta, bf16_to_f(DT[(int64_t)col * lddt + row]), x);
           }
+          const int64_t idx = u.tall ? u.abs + (int64_t)col * u.row_stride + row
+                                     : u.abs + (int64_t)row * u.row_stride + col;
+          w[idx] = fmaf(w[idx], decay, -ls * x);
         }
       }
     }
   }
 }
 
-template <int TILE, bool FINAL>
-hipError_t launch(const GemmArgs &a, int batch, hipStream_t s) {
-  const dim3 grid((unsigned)((a.M / TILE) * (a.N / TILE)), (unsigned)batch);
-  hipLaunchKernelGGL((k_gemm_nt<TILE, FINAL>), grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+struct NsArgs {
+  char *ws;
+  const NsGroupDev *groups;
+  const NsTile *tiles;
+  const float *uscale;
+  const MuonUnit *units;
+  float *w;
+  float lr, decay;          // f2
+  float ca, cb, cc;         // quintic coefficients
+  int iter;
+};
+
+// STAGE: 0 Gram, 1 poly, 2 update, 3 update + f2
+template <int STAGE>
+__global__ __launch_bounds__(256, 2) void k_ns(NsArgs a) {
+  constexpr int TILE = kNsTile;
+  __shared__ __attribute__((aligned(1024))) char smem[smem_bytes<TILE>()];
+  const NsTile tl = a.tiles[blockIdx.x];
+  const NsGroupDev g = a.groups[tl.group];
+  const int unit = g.unit_base + tl.b;
+  const float s = a.uscale[unit];
+  const bool zero = s == 0.f;                       // all-zero momentum: direction is exactly 0
+  if (zero && STAGE != 3) return;
+  const int64_t rp = g.r_pad, cp = g.c_pad;
+  uint16_t *X = reinterpret_cast<uint16_t *>(a.ws + g.off_x) + tl.b * rp * cp;
+  uint16_t *XT0 = reinterpret_cast<uint16_t *>(a.ws + g.off_xt0) + tl.b * rp * cp;
+  uint16_t *XT1 = reinterpret_cast<uint16_t *>(a.ws + g.off_xt1) + tl.b * rp * cp;
+  uint16_t *A = reinterpret_cast<uint16_t *>(a.ws + g.off_a) + tl.b * rp * rp;
+  uint16_t *B = reinterpret_cast<uint16_t *>(a.ws + g.off_b) + tl.b * rp * rp;
+  const int r0 = tl.tm * TILE, c0 = tl.tn * TILE;
+  f32x16_t acc[TILE / 64][TILE / 64];
+  if (STAGE == 0) {
+    gemm_core<TILE>(reinterpret_cast<const char *>(X + r0 * cp), reinterpret_cast<const char *>(X + c0 * cp), cp,
+                    smem, acc);
+    const float al = a.iter == 0 ? s * s : 1.f;
+    store_tile<TILE>(acc, al, 0.f, nullptr, 0, A, rp, tl.tm != tl.tn ? A : nullptr, rp, r0, c0, smem);
+  } else if (STAGE == 1) {
+    gemm_core<TILE>(reinterpret_cast<const char *>(A + r0 * rp), reinterpret_cast<const char *>(A + c0 * rp), rp,
+                    smem, acc);
+    // D = A, read through its transpose (A is symmetric)
+    store_tile<TILE>(acc, a.cc, a.cb, A, rp, B, rp, tl.tm != tl.tn ? B : nullptr, rp, r0, c0, smem);
+  } else {
+    const uint16_t *XTc = (a.iter & 1) ? XT1 : XT0;
+    uint16_t *XTn = (a.iter & 1) ? XT0 : XT1;
+    const float al = a.iter == 0 ? s : 1.f;
+    const float be = a.iter == 0 ? a.ca * s : a.ca;
+    if (STAGE == 2) {
+      gemm_core<TILE>(reinterpret_cast<const char *>(B + r0 * rp), reinterpret_cast<const char *>(XTc + c0 * rp),
+                      rp, smem, acc);
+      // D = X, read through X^T (the Q operand of this product)
+      store_tile<TILE>(acc, al, be, XTc, rp, X, cp, XTn, rp, r0, c0, smem);
+    } else {
+      if (!zero)
+        gemm_core<TILE>(reinterpret_cast<const char *>(B + r0 * rp), reinterpret_cast<const char *>(XTc + c0 * rp),
+                        rp, smem, acc);
+      const MuonUnit u = a.units[unit];
+      final_tile<TILE>(acc, al, be, XTc, rp, u, a.w, a.lr, a.decay, r0, c0, zero);
+    }
+  }
 }
 
-hipError_t dispatch(const GemmArgs &a, int batch, int tile, bool final_, hipStream_t s) {
-  if (tile == 128) return final_ ? launch<128, true>(a, batch, s) : launch<128, false>(a, batch, s);
-  if (tile == 256) return final_ ? launch<256, true>(a, batch, s) : launch<256, false>(a, batch, s);
-  return hipErrorInvalidValue;
+// Raw batched contraction for tests: O[b] = alpha P[b] Q[b]^T + beta D[b].
+struct RawArgs {
+  const uint16_t *P, *Q, *D;
+  uint16_t *O, *OT;
+  int M, N, K;
+  float alpha, beta;
+};
+
+template <int TILE>
+__global__ __launch_bounds__(256, 1) void k_gemm_raw(RawArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[smem_bytes<TILE>()];
+  const int b = blockIdx.y;
+  const int tiles_n = a.N / TILE;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  const int64_t M = a.M, N = a.N, K = a.K;
+  f32x16_t acc[TILE / 64][TILE / 64];
+  gemm_core<TILE>(reinterpret_cast<const char *>(a.P + b * M * K + (int64_t)tm * TILE * K),
+                  reinterpret_cast<const char *>(a.Q + b * N * K + (int64_t)tn * TILE * K), K, smem, acc);
+  // the raw entry takes D^T (N x M), the layout the update product reads X in
+  store_tile<TILE>(acc, a.alpha, a.beta, a.D ? a.D + b * M * N : nullptr, M, a.O + b * M * N, N,
+                   a.OT ? a.OT + b * M * N : nullptr, M, tm * TILE, tn * TILE, smem);
 }
 
 }  // namespace
 
-hipError_t launch_ns_stage(const sshdp_plan &p, const Group &g, int stage, int iter, char *ws, float *w_main,
-                           float lr, float wd, hipStream_t s) {
-  uint16_t *X = reinterpret_cast<uint16_t *>(ws + g.off_x);
-  uint16_t *XT[2] = {reinterpret_cast<uint16_t *>(ws + g.off_xt0), reinterpret_cast<uint16_t *>(ws + g.off_xt1)};
-  uint16_t *A = reinterpret_cast<uint16_t *>(ws + g.off_a);
-  uint16_t *B = reinterpret_cast<uint16_t *>(ws + g.off_b);
-  const int64_t sx = (int64_t)g.r_pad * g.c_pad, sa = (int64_t)g.r_pad * g.r_pad;
-  GemmArgs a{};
+hipError_t launch_ns_stage(const sshdp_plan &p, int stage, int iter, char *ws, float *w_main, float lr, float wd,
+                           hipStream_t s) {
+  const std::vector<NsTile> &list = stage == 0 ? p.ns_gram : stage == 1 ? p.ns_poly : p.ns_update;
+  if (list.empty()) return hipSuccess;
+  NsArgs a{};
+  a.ws = ws;
+  a.groups = p.d.ns_groups;
+  a.tiles = stage == 0 ? p.d.ns_gram : stage == 1 ? p.d.ns_poly : p.d.ns_update;
   a.uscale = reinterpret_cast<const float *>(ws + p.ws_uscale);
-  a.unit_base = g.unit_base;
   a.units = p.d.munits;
   a.w = w_main;
   a.lr = lr;
   a.decay = (float)(1.0 - (double)lr * (double)wd);
-  if (stage == 0) {                       // A = alpha X X^T
-    a.P = a.Q = X; a.sP = a.sQ = sx;
-    a.O = A; a.sO = sa;
-    a.M = a.N = g.r_pad; a.K = g.c_pad;
-    a.alpha = 1.f; a.alpha_pow = iter == 0 ? 2 : 0;
-  } else if (stage == 1) {                // B = c A A + b A
-    a.P = a.Q = A; a.sP = a.sQ = sa;
-    a.D = A; a.sD = sa;
-    a.O = B; a.sO = sa;
-    a.M = a.N = a.K = g.r_pad;
-    a.alpha = p.opts.ns_c; a.beta = p.opts.ns_b;
-  } else {                                // X' = alpha B X + beta X
-    a.P = B; a.sP = sa;
-    a.Q = XT[iter & 1]; a.sQ = sx;
-    a.D = X; a.sD = sx;
-    if (stage == 2) {
-      a.O = X; a.sO = sx;
-      a.OT = XT[(iter + 1) & 1]; a.sOT = sx;
-    }
-    a.M = g.r_pad; a.N = g.c_pad; a.K = g.r_pad;
-    a.alpha = 1.f; a.beta = p.opts.ns_a;
-    a.alpha_pow = a.beta_pow = iter == 0 ? 1 : 0;
+  a.ca = p.opts.ns_a;
+  a.cb = p.opts.ns_b;
+  a.cc = p.opts.ns_c;
+  a.iter = iter;
+  const dim3 grid((unsigned)list.size());
+  switch (stage) {
+    case 0: hipLaunchKernelGGL(k_ns<0>, grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL(k_ns<1>, grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(k_ns<2>, grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL(k_ns<3>, grid, dim3(256), 0, s, a); break;
   }
-  return dispatch(a, g.n, g.tile, stage == 3, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_raw(const void *P, const void *Q, const void *D, void *O, void *OT, int M, int N, int K,
                            int batch, float alpha, float beta, int tile, hipStream_t s) {
-  GemmArgs a{};
+  RawArgs a{};
   a.P = static_cast<const uint16_t *>(P);
   a.Q = static_cast<const uint16_t *>(Q);
   a.D = static_cast<const uint16_t *>(D);
   a.O = static_cast<uint16_t *>(O);
   a.OT = static_cast<uint16_t *>(OT);
-  a.sP = (int64_t)M * K;
-  a.sQ = (int64_t)N * K;
-  a.sD = a.sO = a.sOT = (int64_t)M * N;
   a.M = M; a.N = N; a.K = K;
   a.alpha = alpha; a.beta = beta;
-  return dispatch(a, batch, tile, false, s);
+  if (tile == 128) {
+    hipLaunchKernelGGL(k_gemm_raw<128>, dim3((unsigned)((M / 128) * (N / 128)), (unsigned)batch), dim3(256), 0, s, a);
+  } else if (tile == 256) {
+    hipLaunchKernelGGL(k_gemm_raw<256>, dim3((unsigned)((M / 256) * (N / 256)), (unsigned)batch), dim3(256), 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace sshdp

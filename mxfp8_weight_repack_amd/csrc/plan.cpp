@@ -94,11 +94,6 @@ float scale_factor(int mode, int64_t rows, int64_t cols) {
   return 1.0f;
 }
 
-// GEMM macro-tile edge for a group's oriented shape.
-int pick_tile(int64_t r, int64_t c) {
-  (void)c;
-  return r >= 512 ? 256 : 128;
-}
 
 void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
   std::map<std::pair<int64_t, int64_t>, std::vector<int32_t>> by_shape;  // ordered: deterministic
@@ -121,7 +116,7 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
     Group g{};
     g.r = (int32_t)kv.first.first;
     g.c = (int32_t)kv.first.second;
-    g.tile = pick_tile(g.r, g.c);
+    g.tile = kNsTile;
     g.r_pad = (int32_t)round_up(g.r, g.tile);
     g.c_pad = (int32_t)round_up(g.c, g.tile);
     g.n = (int32_t)kv.second.size();
@@ -173,6 +168,36 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
     }
   }
   p.ws_bytes = off;
+  // per-stage tile tables: symmetric Gram/poly take tm <= tn; longest K first
+  for (size_t gi = 0; gi < p.groups.size(); ++gi) {
+    const Group &g = p.groups[gi];
+    p.ns_groups.push_back({(int64_t)g.off_x, (int64_t)g.off_xt0, (int64_t)g.off_xt1, (int64_t)g.off_a,
+                           (int64_t)g.off_b, g.r_pad, g.c_pad, g.unit_base, g.n});
+    const int ntr = g.r_pad / kNsTile, ntc = g.c_pad / kNsTile;
+    for (int b = 0; b < g.n; ++b) {
+      for (int tm = 0; tm < ntr; ++tm)
+        for (int tn = tm; tn < ntr; ++tn) {
+          p.ns_gram.push_back({(int32_t)gi, b, tm, tn});
+          p.ns_poly.push_back({(int32_t)gi, b, tm, tn});
+        }
+      for (int tm = 0; tm < ntr; ++tm)
+        for (int tn = 0; tn < ntc; ++tn) p.ns_update.push_back({(int32_t)gi, b, tm, tn});
+    }
+  }
+  auto by_k = [&](std::vector<NsTile> &v, bool gram) {
+    std::stable_sort(v.begin(), v.end(), [&](const NsTile &x, const NsTile &y) {
+      const Group &gx = p.groups[x.group], &gy = p.groups[y.group];
+      return (gram ? gx.c_pad : gx.r_pad) > (gram ? gy.c_pad : gy.r_pad);
+    });
+  };
+  by_k(p.ns_gram, true);
+  by_k(p.ns_poly, false);
+  by_k(p.ns_update, false);
+  const double t3 = (double)kNsTile * kNsTile * 2.0;
+  for (const NsTile &x : p.ns_gram) p.stats.ns_tile_flops += t3 * p.groups[x.group].c_pad;
+  for (const NsTile &x : p.ns_poly) p.stats.ns_tile_flops += t3 * p.groups[x.group].r_pad;
+  for (const NsTile &x : p.ns_update) p.stats.ns_tile_flops += t3 * p.groups[x.group].r_pad;
+  p.stats.ns_tile_flops *= p.opts.ns_steps;
   p.stats.n_muon_units = (int32_t)p.munits.size();
   p.stats.n_groups = (int32_t)p.groups.size();
 }
@@ -272,7 +297,9 @@ size_t table_bytes(const std::vector<T> &v) { return round_up((int64_t)(v.size()
 
 int upload(sshdp_plan &p) {
   const size_t total = table_bytes(p.munits) + table_bytes(p.f0tiles) + table_bytes(p.aseg_all) +
-                       table_bytes(p.aseg_unfused) + table_bytes(p.qregions) + table_bytes(p.qchunks) + 256;
+                       table_bytes(p.aseg_unfused) + table_bytes(p.qregions) + table_bytes(p.qchunks) +
+                       table_bytes(p.ns_groups) + table_bytes(p.ns_gram) + table_bytes(p.ns_poly) +
+                       table_bytes(p.ns_update) + 256;
   if (hipGetDevice(&p.device) != hipSuccess) return SSHDP_ERR_HIP;
   if (hipMalloc(&p.dblock, total) != hipSuccess) { p.dblock = nullptr; return SSHDP_ERR_HIP; }
   std::vector<char> host(total, 0);
@@ -289,6 +316,10 @@ int upload(sshdp_plan &p) {
   put(p.aseg_unfused, p.d.aseg_unfused);
   put(p.qregions, p.d.qregions);
   put(p.qchunks, p.d.qchunks);
+  put(p.ns_groups, p.d.ns_groups);
+  put(p.ns_gram, p.d.ns_gram);
+  put(p.ns_poly, p.d.ns_poly);
+  put(p.ns_update, p.d.ns_update);
   if (hipMemcpy(p.dblock, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) return SSHDP_ERR_HIP;
   return SSHDP_OK;
 }

@@ -49,7 +49,8 @@ def test_gemm_nt_against_fp64(tile, M, N, K, batch):
     Q = r.standard_normal((batch, N, K)).astype(np.float32)
     D = r.standard_normal((batch, M, N)).astype(np.float32)
     bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).cuda()
-    tP, tQ, tD = bf(P), bf(Q), bf(D)
+    tP, tQ = bf(P), bf(Q)
+    tD = bf(np.ascontiguousarray(D.transpose(0, 2, 1)))          # the entry takes D transposed
     O = torch.zeros(batch, M, N, dtype=torch.bfloat16, device="cuda")
     OT = torch.zeros(batch, N, M, dtype=torch.bfloat16, device="cuda")
     sh.gemm_bf16_nt(tP, tQ, tD, O, OT, M, N, K, batch, 0.75, -1.5, tile,
