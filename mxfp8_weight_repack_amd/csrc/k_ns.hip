@@ -37,6 +37,7 @@
 
 #include "internal.h"
 #include "mx_codec.h"
+#include "tile_map.h"
 
 namespace sshdp {
 namespace {
@@ -318,8 +319,8 @@ template <int TILE>
 __global__ __launch_bounds__(256, 1) void k_gemm_raw(RawArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[smem_bytes<TILE>()];
   const int b = blockIdx.y;
-  const int tiles_n = a.N / TILE;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  int tm, tn;
+  xcd_tile((int)blockIdx.x, a.M / TILE, a.N / TILE, &tm, &tn);
   const int64_t M = a.M, N = a.N, K = a.K;
   f32x16_t acc[TILE / 64][TILE / 64];
   gemm_core<TILE>(reinterpret_cast<const char *>(a.P + b * M * K + (int64_t)tm * TILE * K),

@@ -12,6 +12,7 @@
 #include <cmath>
 #include <cstring>
 #include <map>
+#include <tuple>
 #include <new>
 #include <utility>
 
@@ -94,6 +95,54 @@ float scale_factor(int mode, int64_t rows, int64_t cols) {
   return 1.0f;
 }
 
+
+// Order one stage's tiles for the 8 XCDs of an MI355X (workgroup id i runs on
+// XCD i % 8, each XCD with its own L2): tiles are cut into 8 x 8 super-tiles
+// per unit, super-tiles are dealt to XCDs, and each XCD's queue is laid out on
+// the positions i = x (mod 8).  Workgroups that run together on one XCD then
+// share their operand rows and columns through that L2.  Tiles of equal K are
+// ordered among themselves only (longer-K tiles stay first).
+void xcd_order(std::vector<NsTile> &v, const std::vector<Group> &groups, bool gram) {
+  constexpr int kXcd = 8, kSuper = 8;
+  size_t s = 0;
+  while (s < v.size()) {
+    auto kof = [&](const NsTile &t) { return gram ? groups[t.group].c_pad : groups[t.group].r_pad; };
+    size_t e = s;
+    while (e < v.size() && kof(v[e]) == kof(v[s])) ++e;
+    // super-tiles in first-appearance order
+    std::map<std::tuple<int, int, int, int>, size_t> idx;
+    std::vector<std::vector<NsTile>> st;
+    for (size_t i = s; i < e; ++i) {
+      const auto key = std::make_tuple(v[i].group, v[i].b, v[i].tm / kSuper, v[i].tn / kSuper);
+      auto it = idx.find(key);
+      if (it == idx.end()) {
+        idx[key] = st.size();
+        st.push_back({v[i]});
+      } else {
+        st[it->second].push_back(v[i]);
+      }
+    }
+    std::vector<std::vector<NsTile>> q(kXcd);
+    for (auto &sup : st) {                           // deal to the least-loaded XCD
+      size_t best = 0;
+      for (size_t x = 1; x < q.size(); ++x)
+        if (q[x].size() < q[best].size()) best = x;
+      q[best].insert(q[best].end(), sup.begin(), sup.end());
+    }
+    std::vector<size_t> head(kXcd, 0);
+    for (size_t pos = s; pos < e; ++pos) {
+      size_t x = pos % kXcd;
+      if (head[x] >= q[x].size()) {                  // this XCD's queue ran dry: take from the fullest
+        size_t best = x;
+        for (size_t y = 0; y < q.size(); ++y)
+          if (q[y].size() - head[y] > q[best].size() - head[best]) best = y;
+        x = best;
+      }
+      v[pos] = q[x][head[x]++];
+    }
+    s = e;
+  }
+}
 
 void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
   std::map<std::pair<int64_t, int64_t>, std::vector<int32_t>> by_shape;  // ordered: deterministic
@@ -193,6 +242,9 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
   by_k(p.ns_gram, true);
   by_k(p.ns_poly, false);
   by_k(p.ns_update, false);
+  xcd_order(p.ns_gram, p.groups, true);
+  xcd_order(p.ns_poly, p.groups, false);
+  xcd_order(p.ns_update, p.groups, false);
   const double t3 = (double)kNsTile * kNsTile * 2.0;
   for (const NsTile &x : p.ns_gram) p.stats.ns_tile_flops += t3 * p.groups[x.group].c_pad;
   for (const NsTile &x : p.ns_poly) p.stats.ns_tile_flops += t3 * p.groups[x.group].r_pad;

@@ -114,3 +114,35 @@ def test_bf16_bits_equal_torch(codec):
         nan = np.isnan(bits.view(np.float32))
         assert np.array_equal(out[~nan], ref[~nan])
         assert np.all(((out[nan] & 0x7F80) == 0x7F80) & ((out[nan] & 0x7F) != 0))
+
+
+TILEMAP_SHIM = r"""
+#include "tile_map.h"
+int check(int tm_n, int tn_n, int *seen) {
+  for (int p = 0; p < tm_n * tn_n; ++p) {
+    int tm, tn;
+    xcd_tile(p, tm_n, tn_n, &tm, &tn);
+    if (tm < 0 || tm >= tm_n || tn < 0 || tn >= tn_n) return -1;
+    if (seen[tm * tn_n + tn]++) return -2;
+  }
+  return 0;
+}
+"""
+
+
+def test_xcd_tile_map_is_an_in_bounds_bijection(tmp_path):
+    """The raw contraction's workgroup -> tile map (csrc/tile_map.h), compiled
+    for the host: every grid it can be launched with maps onto its tiles
+    exactly once and never outside them."""
+    src = tmp_path / "tm.c"
+    src.write_text(TILEMAP_SHIM)
+    so = tmp_path / "tm.so"
+    subprocess.run(["gcc", "-O1", "-shared", "-fPIC", "-I", CSRC, str(src), "-o", str(so)], check=True)
+    L = ctypes.CDLL(str(so))
+    L.check.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    dims = sorted(set([1, 2, 3, 4, 7, 8, 12, 16, 24, 32, 40, 56, 64, 72, 88, 96, 128, 224]))
+    for m in dims:
+        for n in dims:
+            seen = np.zeros(m * n, np.int32)
+            assert L.check(m, n, seen.ctypes.data) == 0, (m, n)
+            assert np.all(seen == 1), (m, n)
