@@ -170,7 +170,8 @@ typedef struct {
   int32_t r, c;               /* oriented shape                                            */
   int32_t r_pad, c_pad;       /* padded to the GEMM tile                                   */
   int32_t n_units;
-  int32_t tile;               /* GEMM macro-tile edge used for this group                  */
+  int32_t tile;               /* macro-tile edge of the update product (128 or 256)        */
+  int32_t tile_gram;          /* macro-tile edge of the Gram and polynomial products       */
 } sshdp_group_info;
 
 /* Fill *opts with the defaults above. */

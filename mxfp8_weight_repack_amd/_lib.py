@@ -70,7 +70,8 @@ class PlanStats(ctypes.Structure):
 
 class GroupInfo(ctypes.Structure):
     _fields_ = [("r", ctypes.c_int32), ("c", ctypes.c_int32), ("r_pad", ctypes.c_int32),
-                ("c_pad", ctypes.c_int32), ("n_units", ctypes.c_int32), ("tile", ctypes.c_int32)]
+                ("c_pad", ctypes.c_int32), ("n_units", ctypes.c_int32), ("tile", ctypes.c_int32),
+                ("tile_gram", ctypes.c_int32)]
 
 
 # every symbol include/sshdp.h declares, with its argument and return types

@@ -12,7 +12,8 @@
 namespace sshdp {
 
 constexpr int kF0Tile = 64;          // f0 transposing tile edge (elements)
-constexpr int kNsTile = 128;         // Newton-Schulz GEMM macro-tile edge (elements)
+constexpr int kNsSmall = 128;        // Newton-Schulz GEMM macro tiles: 128 x 128 (4 waves) ...
+constexpr int kNsLarge = 256;        // ... or 256 x 256 (8 waves), chosen per group and stage
 constexpr int kChunk = 4096;         // elements per AdamW / requant work item
 constexpr size_t kAlign = 256;       // workspace sub-buffer alignment (bytes)
 
@@ -41,7 +42,8 @@ struct F0Tile {
 
 // Newton-Schulz group: units with the same oriented shape r x c (r <= c).
 struct Group {
-  int32_t r, c, r_pad, c_pad, n, tile;
+  int32_t r, c, r_pad, c_pad, n;
+  int32_t tile_g, tile_u;   // macro tile of the Gram/poly products and of the update product
   int32_t unit_base;    // first MuonUnit of the group in the device table
   size_t off_x, off_xt0, off_xt1, off_a, off_b;   // workspace byte offsets
 };
@@ -89,9 +91,7 @@ struct DeviceTables {
   QRegion *qregions = nullptr;
   QChunk *qchunks = nullptr;
   NsGroupDev *ns_groups = nullptr;
-  NsTile *ns_gram = nullptr;
-  NsTile *ns_poly = nullptr;
-  NsTile *ns_update = nullptr;
+  NsTile *ns_tiles[3][2] = {};   // [stage: Gram, poly, update][tile: 128, 256]
 };
 
 }  // namespace sshdp
@@ -105,7 +105,7 @@ struct sshdp_plan {
   std::vector<sshdp::F0Tile> f0tiles;
   std::vector<sshdp::Group> groups;
   std::vector<sshdp::NsGroupDev> ns_groups;
-  std::vector<sshdp::NsTile> ns_gram, ns_poly, ns_update;   // per-stage tile tables, longest K first
+  std::vector<sshdp::NsTile> ns_tiles[3][2];   // per stage and tile size, longest K first
   std::vector<sshdp::ASeg> aseg_all, aseg_unfused;
   std::vector<sshdp::QRegion> qregions;
   std::vector<sshdp::QChunk> qchunks;   // fused-eligible chunks first

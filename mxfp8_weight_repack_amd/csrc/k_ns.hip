@@ -47,84 +47,97 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BK = 64;             // K elements per LDS stage
 
-// LDS bytes a TILE kernel needs: the double-buffered operand stages, or the
-// epilogue's padded bf16 tile, whichever is larger
-template <int TILE>
-constexpr int smem_bytes() {
-  return 4 * TILE * BK * 2 > TILE * (TILE + 8) * 2 ? 4 * TILE * BK * 2 : TILE * (TILE + 8) * 2;
-}
-
 __device__ __forceinline__ float bf16_to_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// Tile configuration: TM x TN output per workgroup of WM x WN waves, each
+// wave (TM/WM) x (TN/WN) as 32x32 MFMA blocks.
+template <int TM_, int TN_, int WM_, int WN_>
+struct Cfg {
+  static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+  static constexpr int NW = WM * WN, NT = 64 * NW;
+  static constexpr int WTM = TM / WM, WTN = TN / WN;
+  static constexpr int MBM = WTM / 32, MBN = WTN / 32;
+  static constexpr int SEGA = TM * BK * 2, SEGB = TN * BK * 2;     // bytes of one operand stage
+  static constexpr int NIA = TM / (8 * NW), NIB = TN / (8 * NW);   // DMA instructions per thread
+  static constexpr int STAGE = SEGA + SEGB;
+  static constexpr int LDS = 2 * STAGE > TM * (TN + 8) * 2 ? 2 * STAGE : TM * (TN + 8) * 2;
+  static_assert(NW % 4 == 0 && NIA >= 1 && NIB >= 1, "tile config");
+};
+
 // Physical 16-byte chunk = logical chunk ^ swz(row): any 8 consecutive rows
-// (and any 16) read at one logical chunk land on distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// (and any 16) of a 32-row block read at one logical chunk land on distinct
+// 16-byte bank groups.
+__device__ __forceinline__ int swz(int r) { return ((r & 31) ^ ((r & 31) >> 3)) & 7; }
 
-// C[TILE x TILE] = P[TILE x K] Q[TILE x K]^T, P and Q row-major with row pitch
-// K elements (bf16), starting at byte addresses gP, gQ (uniform).
-template <int TILE>
+// acc = P[TM x K] Q[TN x K]^T, P and Q row-major with row pitch K elements
+// (bf16) starting at byte addresses gP, gQ (uniform).
+template <class C>
 __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_t K, char *smem,
-                                          f32x16_t (&acc)[TILE / 64][TILE / 64]) {
-  constexpr int WT = TILE / 2, MB = WT / 32;
-  constexpr int SEG = TILE * BK * 2;                 // bytes of one operand tile
-  constexpr int NI = TILE / 32;                      // DMA instructions per thread per operand
+                                          f32x16_t (&acc)[C::MBM][C::MBN]) {
+  constexpr int MBM = C::MBM, MBN = C::MBN, NW = C::NW;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WN, wn = wave % C::WN;
 
-  // DMA: instruction i of wave w fills rows 8*(4i + w) .. +7, 8 lanes per row;
+  // DMA: instruction i of wave w fills rows 8*(NW*i + w) .. +7, 8 lanes per row;
   // lane i of an instruction lands at LDS base + 16*i
   const int drow = 8 * wave + (lane >> 3);
-  const int dchunk = (lane & 7) ^ swz(drow);         // rows drow + 32 i share the swizzle
+  const int dchunk = (lane & 7) ^ swz(drow);         // rows drow + 8*NW*i share the swizzle
   const uint32_t loff = (uint32_t)(drow * K + dchunk * 8) * 2u;
   const int dlds = wave * 1024;
 
   // fragment reads: lane holds row (lane & 31) of a 32-row block, logical chunk 2 kk + (lane >> 5)
   const int lrow = lane & 31;
-  const int ra = (wm * WT + lrow) * 128, rb = (wn * WT + lrow) * 128;
+  const int ra = (wm * C::WTM + lrow) * 128, rb = (wn * C::WTN + lrow) * 128;
   int cofs[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) cofs[kk] = ((2 * kk + (lane >> 5)) ^ swz(lrow)) * 16;
 
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+  for (int i = 0; i < MBM; ++i)
 #pragma unroll
-    for (int j = 0; j < MB; ++j)
+    for (int j = 0; j < MBN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   auto dma = [&](int stage, int64_t k0) __attribute__((always_inline)) {
-    char *sa = smem + stage * 2 * SEG;
+    char *sa = smem + stage * C::STAGE;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int64_t ob = ((int64_t)i * 32 * K + k0) * 2;
+    for (int i = 0; i < C::NIA; ++i) {
+      const int64_t ob = ((int64_t)i * 8 * NW * K + k0) * 2;
       __builtin_amdgcn_global_load_lds(gP + ob + loff,
-                                       (__attribute__((address_space(3))) void *)(sa + dlds + i * 4096), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(gQ + ob + loff,
-                                       (__attribute__((address_space(3))) void *)(sa + SEG + dlds + i * 4096), 16, 0,
+                                       (__attribute__((address_space(3))) void *)(sa + dlds + i * NW * 1024), 16, 0,
                                        0);
     }
+#pragma unroll
+    for (int i = 0; i < C::NIB; ++i) {
+      const int64_t ob = ((int64_t)i * 8 * NW * K + k0) * 2;
+      __builtin_amdgcn_global_load_lds(gQ + ob + loff,
+                                       (__attribute__((address_space(3))) void *)(sa + C::SEGA + dlds + i * NW * 1024),
+                                       16, 0, 0);
+    }
   };
-  bf16x8_t fa0[MB], fb0[MB], fa1[MB], fb1[MB];
-  auto ldfrag = [&](const char *sa, int kk, bf16x8_t(&fa_)[MB], bf16x8_t(&fb_)[MB]) __attribute__((always_inline)) {
+  bf16x8_t fa0[MBM], fb0[MBN], fa1[MBM], fb1[MBN];
+  auto ldfrag = [&](const char *sa, int kk, bf16x8_t(&fa_)[MBM], bf16x8_t(&fb_)[MBN]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < MB; ++i) fa_[i] = *reinterpret_cast<const bf16x8_t *>(sa + ra + i * 32 * 128 + cofs[kk]);
+    for (int i = 0; i < MBM; ++i) fa_[i] = *reinterpret_cast<const bf16x8_t *>(sa + ra + i * 32 * 128 + cofs[kk]);
 #pragma unroll
-    for (int j = 0; j < MB; ++j)
-      fb_[j] = *reinterpret_cast<const bf16x8_t *>(sa + SEG + rb + j * 32 * 128 + cofs[kk]);
+    for (int j = 0; j < MBN; ++j)
+      fb_[j] = *reinterpret_cast<const bf16x8_t *>(sa + C::SEGA + rb + j * 32 * 128 + cofs[kk]);
   };
-  auto mma = [&](bf16x8_t(&fa_)[MB], bf16x8_t(&fb_)[MB]) __attribute__((always_inline)) {
+  auto mma = [&](bf16x8_t(&fa_)[MBM], bf16x8_t(&fb_)[MBN]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+    for (int i = 0; i < MBM; ++i)
 #pragma unroll
-      for (int j = 0; j < MB; ++j)
+      for (int j = 0; j < MBN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_[i], fb_[j], acc[i][j], 0, 0, 0);
     // each MFMA followed by one fragment read of the next slice
+    constexpr int NR = MBM + MBN, NM = MBM * MBN;
 #pragma unroll
-    for (int i = 0; i < 2 * MB; ++i) {
+    for (int i = 0; i < (NR < NM ? NR : NM); ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    if (MB * MB > 2 * MB) __builtin_amdgcn_sched_group_barrier(0x008, MB * MB - 2 * MB, 0);
+    if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
   };
 
   const int nk = (int)(K / BK);
@@ -135,7 +148,7 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
     if (kt + 1 < nk) dma(st ^ 1, (int64_t)(kt + 1) * BK);
-    const char *sa = smem + st * 2 * SEG;
+    const char *sa = smem + st * C::STAGE;
     ldfrag(sa, 1, fa1, fb1);
     mma(fa0, fb0);
     ldfrag(sa, 2, fa0, fb0);
@@ -144,35 +157,35 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
     mma(fa0, fb0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kt + 1 < nk) ldfrag(smem + (st ^ 1) * 2 * SEG, 0, fa0, fb0);
+    if (kt + 1 < nk) ldfrag(smem + (st ^ 1) * C::STAGE, 0, fa0, fb0);
     mma(fa1, fb1);
   }
 }
 
-// Epilogue of a TILE x TILE product: x = alpha*acc + beta*D, rounded to bf16,
+// Epilogue of a TM x TN product: x = alpha*acc + beta*D, rounded to bf16,
 // stored row-major to O (leading dim ldo) and, if OT, transposed to OT[col*ldt + row].
 // D is read through its transpose DT (DT[col*lddt + row] = D[row][col]): element
 // (m, n) of a 32x32 MFMA block sits in lane n + 32*((m/4)%2), register
 // (m/8)*4 + m%4, so a lane holds 4 consecutive rows of one column and both the
 // D^T read and the O^T write are 8 contiguous bytes.  The row-major O store goes
 // through LDS (bf16 tile, padded rows) so each lane writes 16 contiguous bytes.
-// smem must be free (all fragment reads done) and hold TILE*(TILE+8)*2 bytes.
-template <int TILE>
-__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TILE / 64][TILE / 64], float alpha, float beta,
+// smem must be free (all fragment reads done) and hold TM*(TN+8)*2 bytes.
+template <class C>
+__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[C::MBM][C::MBN], float alpha, float beta,
                                            const uint16_t *DT, int64_t lddt, uint16_t *O, int64_t ldo, uint16_t *OT,
                                            int64_t ldt, int r0, int c0, char *smem) {
-  constexpr int WT = TILE / 2, MB = WT / 32, LP = TILE + 8;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
+  constexpr int LP = C::TN + 8;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave / C::WN, wn = wave % C::WN;
   uint16_t *lt = reinterpret_cast<uint16_t *>(smem);
 #pragma unroll
-  for (int i = 0; i < MB; ++i) {
+  for (int i = 0; i < C::MBM; ++i) {
 #pragma unroll
-    for (int j = 0; j < MB; ++j) {
-      const int lc = wn * WT + j * 32 + (lane & 31);
+    for (int j = 0; j < C::MBN; ++j) {
+      const int lc = wn * C::WTN + j * 32 + (lane & 31);
       const int col = c0 + lc;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int lr0 = wm * WT + i * 32 + g4 * 8 + (lane >> 5) * 4;
+        const int lr0 = wm * C::WTM + i * 32 + g4 * 8 + (lane >> 5) * 4;
         const int row0 = r0 + lr0;
         float x[4];
 #pragma unroll
@@ -200,10 +213,10 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TILE / 64][TILE
     }
   }
   __syncthreads();
-  constexpr int CH = TILE / 8;                       // 16-byte chunks per row
+  constexpr int CH = C::TN / 8;                      // 16-byte chunks per row
 #pragma unroll
-  for (int k = 0; k < TILE * CH / 256; ++k) {
-    const int id = t + 256 * k, row = id / CH, ch = id - row * CH;
+  for (int k = 0; k < C::TM * CH / C::NT; ++k) {
+    const int id = t + C::NT * k, row = id / CH, ch = id - row * CH;
     const uint4 v = *reinterpret_cast<const uint4 *>(&lt[row * LP + ch * 8]);
     *reinterpret_cast<uint4 *>(O + (int64_t)(r0 + row) * ldo + c0 + ch * 8) = v;
   }
@@ -211,23 +224,22 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TILE / 64][TILE
 
 // f2 on a tile of the last update product: w <- w*decay - lr*scale*x for the
 // elements inside the unit (oriented r x c; a tall unit's view is the transpose).
-template <int TILE>
-__device__ __forceinline__ void final_tile(const f32x16_t (&acc)[TILE / 64][TILE / 64], float alpha, float beta,
+template <class C>
+__device__ __forceinline__ void final_tile(const f32x16_t (&acc)[C::MBM][C::MBN], float alpha, float beta,
                                            const uint16_t *DT, int64_t lddt, const MuonUnit &u, float *w, float lr,
                                            float decay, int r0, int c0, bool zero) {
-  constexpr int WT = TILE / 2, MB = WT / 32;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const int r_unit = u.tall ? u.cols : u.rows, c_unit = u.tall ? u.rows : u.cols;
   const float ls = lr * u.upd_scale;
 #pragma unroll
-  for (int i = 0; i < MB; ++i) {
+  for (int i = 0; i < C::MBM; ++i) {
 #pragma unroll
-    for (int j = 0; j < MB; ++j) {
-      const int col = c0 + wn * WT + j * 32 + (lane & 31);
+    for (int j = 0; j < C::MBN; ++j) {
+      const int col = c0 + wn * C::WTN + j * 32 + (lane & 31);
       if (col >= c_unit) continue;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int row0 = r0 + wm * WT + i * 32 + g4 * 8 + (lane >> 5) * 4;
+        const int row0 = r0 + wm * C::WTM + i * 32 + g4 * 8 + (lane >> 5) * 4;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int row = row0 + q;
@@ -259,10 +271,10 @@ struct NsArgs {
 };
 
 // STAGE: 0 Gram, 1 poly, 2 update, 3 update + f2
-template <int STAGE>
-__global__ __launch_bounds__(256, 2) void k_ns(NsArgs a) {
-  constexpr int TILE = kNsTile;
-  __shared__ __attribute__((aligned(1024))) char smem[smem_bytes<TILE>()];
+template <int STAGE, class C>
+__global__ __launch_bounds__(C::NT, C::NT == 256 ? 2 : 1) void k_ns(NsArgs a) {
+  constexpr int TILE = C::TM;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   const NsTile tl = a.tiles[blockIdx.x];
   const NsGroupDev g = a.groups[tl.group];
   const int unit = g.unit_base + tl.b;
@@ -276,33 +288,33 @@ __global__ __launch_bounds__(256, 2) void k_ns(NsArgs a) {
   uint16_t *A = reinterpret_cast<uint16_t *>(a.ws + g.off_a) + tl.b * rp * rp;
   uint16_t *B = reinterpret_cast<uint16_t *>(a.ws + g.off_b) + tl.b * rp * rp;
   const int r0 = tl.tm * TILE, c0 = tl.tn * TILE;
-  f32x16_t acc[TILE / 64][TILE / 64];
+  f32x16_t acc[C::MBM][C::MBN];
   if (STAGE == 0) {
-    gemm_core<TILE>(reinterpret_cast<const char *>(X + r0 * cp), reinterpret_cast<const char *>(X + c0 * cp), cp,
+    gemm_core<C>(reinterpret_cast<const char *>(X + r0 * cp), reinterpret_cast<const char *>(X + c0 * cp), cp,
                     smem, acc);
     const float al = a.iter == 0 ? s * s : 1.f;
-    store_tile<TILE>(acc, al, 0.f, nullptr, 0, A, rp, tl.tm != tl.tn ? A : nullptr, rp, r0, c0, smem);
+    store_tile<C>(acc, al, 0.f, nullptr, 0, A, rp, tl.tm != tl.tn ? A : nullptr, rp, r0, c0, smem);
   } else if (STAGE == 1) {
-    gemm_core<TILE>(reinterpret_cast<const char *>(A + r0 * rp), reinterpret_cast<const char *>(A + c0 * rp), rp,
+    gemm_core<C>(reinterpret_cast<const char *>(A + r0 * rp), reinterpret_cast<const char *>(A + c0 * rp), rp,
                     smem, acc);
     // D = A, read through its transpose (A is symmetric)
-    store_tile<TILE>(acc, a.cc, a.cb, A, rp, B, rp, tl.tm != tl.tn ? B : nullptr, rp, r0, c0, smem);
+    store_tile<C>(acc, a.cc, a.cb, A, rp, B, rp, tl.tm != tl.tn ? B : nullptr, rp, r0, c0, smem);
   } else {
     const uint16_t *XTc = (a.iter & 1) ? XT1 : XT0;
     uint16_t *XTn = (a.iter & 1) ? XT0 : XT1;
     const float al = a.iter == 0 ? s : 1.f;
     const float be = a.iter == 0 ? a.ca * s : a.ca;
     if (STAGE == 2) {
-      gemm_core<TILE>(reinterpret_cast<const char *>(B + r0 * rp), reinterpret_cast<const char *>(XTc + c0 * rp),
+      gemm_core<C>(reinterpret_cast<const char *>(B + r0 * rp), reinterpret_cast<const char *>(XTc + c0 * rp),
                       rp, smem, acc);
       // D = X, read through X^T (the Q operand of this product)
-      store_tile<TILE>(acc, al, be, XTc, rp, X, cp, XTn, rp, r0, c0, smem);
+      store_tile<C>(acc, al, be, XTc, rp, X, cp, XTn, rp, r0, c0, smem);
     } else {
       if (!zero)
-        gemm_core<TILE>(reinterpret_cast<const char *>(B + r0 * rp), reinterpret_cast<const char *>(XTc + c0 * rp),
+        gemm_core<C>(reinterpret_cast<const char *>(B + r0 * rp), reinterpret_cast<const char *>(XTc + c0 * rp),
                         rp, smem, acc);
       const MuonUnit u = a.units[unit];
-      final_tile<TILE>(acc, al, be, XTc, rp, u, a.w, a.lr, a.decay, r0, c0, zero);
+      final_tile<C>(acc, al, be, XTc, rp, u, a.w, a.lr, a.decay, r0, c0, zero);
     }
   }
 }
@@ -315,31 +327,52 @@ struct RawArgs {
   float alpha, beta;
 };
 
-template <int TILE>
-__global__ __launch_bounds__(256, 1) void k_gemm_raw(RawArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[smem_bytes<TILE>()];
+template <class C>
+__global__ __launch_bounds__(C::NT, 1) void k_gemm_raw(RawArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   const int b = blockIdx.y;
   int tm, tn;
-  xcd_tile((int)blockIdx.x, a.M / TILE, a.N / TILE, &tm, &tn);
+  xcd_tile((int)blockIdx.x, a.M / C::TM, a.N / C::TN, &tm, &tn);
   const int64_t M = a.M, N = a.N, K = a.K;
-  f32x16_t acc[TILE / 64][TILE / 64];
-  gemm_core<TILE>(reinterpret_cast<const char *>(a.P + b * M * K + (int64_t)tm * TILE * K),
-                  reinterpret_cast<const char *>(a.Q + b * N * K + (int64_t)tn * TILE * K), K, smem, acc);
+  f32x16_t acc[C::MBM][C::MBN];
+  gemm_core<C>(reinterpret_cast<const char *>(a.P + b * M * K + (int64_t)tm * C::TM * K),
+               reinterpret_cast<const char *>(a.Q + b * N * K + (int64_t)tn * C::TN * K), K, smem, acc);
   // the raw entry takes D^T (N x M), the layout the update product reads X in
-  store_tile<TILE>(acc, a.alpha, a.beta, a.D ? a.D + b * M * N : nullptr, M, a.O + b * M * N, N,
-                   a.OT ? a.OT + b * M * N : nullptr, M, tm * TILE, tn * TILE, smem);
+  store_tile<C>(acc, a.alpha, a.beta, a.D ? a.D + b * M * N : nullptr, M, a.O + b * M * N, N,
+                a.OT ? a.OT + b * M * N : nullptr, M, tm * C::TM, tn * C::TN, smem);
+}
+
+using CSmall = Cfg<kNsSmall, kNsSmall, 2, 2>;   // 4 waves, two workgroups per CU
+using CLarge = Cfg<kNsLarge, kNsLarge, 2, 4>;   // 8 waves (two per SIMD), one workgroup per CU
+
+template <int STAGE, class C>
+hipError_t launch_list(const NsArgs &a, size_t n, hipStream_t s) {
+  hipLaunchKernelGGL((k_ns<STAGE, C>), dim3((unsigned)n), dim3(C::NT), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int STAGE>
+hipError_t launch_sizes(const sshdp_plan &p, NsArgs a, int st, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (!p.ns_tiles[st][1].empty()) {           // 256-tile work first: it is the long part
+    a.tiles = p.d.ns_tiles[st][1];
+    e = launch_list<STAGE, CLarge>(a, p.ns_tiles[st][1].size(), s);
+    if (e != hipSuccess) return e;
+  }
+  if (!p.ns_tiles[st][0].empty()) {
+    a.tiles = p.d.ns_tiles[st][0];
+    e = launch_list<STAGE, CSmall>(a, p.ns_tiles[st][0].size(), s);
+  }
+  return e;
 }
 
 }  // namespace
 
 hipError_t launch_ns_stage(const sshdp_plan &p, int stage, int iter, char *ws, float *w_main, float lr, float wd,
                            hipStream_t s) {
-  const std::vector<NsTile> &list = stage == 0 ? p.ns_gram : stage == 1 ? p.ns_poly : p.ns_update;
-  if (list.empty()) return hipSuccess;
   NsArgs a{};
   a.ws = ws;
   a.groups = p.d.ns_groups;
-  a.tiles = stage == 0 ? p.d.ns_gram : stage == 1 ? p.d.ns_poly : p.d.ns_update;
   a.uscale = reinterpret_cast<const float *>(ws + p.ws_uscale);
   a.units = p.d.munits;
   a.w = w_main;
@@ -349,14 +382,12 @@ hipError_t launch_ns_stage(const sshdp_plan &p, int stage, int iter, char *ws, f
   a.cb = p.opts.ns_b;
   a.cc = p.opts.ns_c;
   a.iter = iter;
-  const dim3 grid((unsigned)list.size());
   switch (stage) {
-    case 0: hipLaunchKernelGGL(k_ns<0>, grid, dim3(256), 0, s, a); break;
-    case 1: hipLaunchKernelGGL(k_ns<1>, grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(k_ns<2>, grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL(k_ns<3>, grid, dim3(256), 0, s, a); break;
+    case 0: return launch_sizes<0>(p, a, 0, s);
+    case 1: return launch_sizes<1>(p, a, 1, s);
+    case 2: return launch_sizes<2>(p, a, 2, s);
+    default: return launch_sizes<3>(p, a, 2, s);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_gemm_raw(const void *P, const void *Q, const void *D, void *O, void *OT, int M, int N, int K,
@@ -370,9 +401,11 @@ hipError_t launch_gemm_raw(const void *P, const void *Q, const void *D, void *O,
   a.M = M; a.N = N; a.K = K;
   a.alpha = alpha; a.beta = beta;
   if (tile == 128) {
-    hipLaunchKernelGGL(k_gemm_raw<128>, dim3((unsigned)((M / 128) * (N / 128)), (unsigned)batch), dim3(256), 0, s, a);
+    using C = CSmall;
+    hipLaunchKernelGGL(k_gemm_raw<C>, dim3((unsigned)((M / 128) * (N / 128)), (unsigned)batch), dim3(C::NT), 0, s, a);
   } else if (tile == 256) {
-    hipLaunchKernelGGL(k_gemm_raw<256>, dim3((unsigned)((M / 256) * (N / 256)), (unsigned)batch), dim3(256), 0, s, a);
+    using C = CLarge;
+    hipLaunchKernelGGL(k_gemm_raw<C>, dim3((unsigned)((M / 256) * (N / 256)), (unsigned)batch), dim3(C::NT), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -165,9 +165,17 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
     Group g{};
     g.r = (int32_t)kv.first.first;
     g.c = (int32_t)kv.first.second;
-    g.tile = kNsTile;
-    g.r_pad = (int32_t)round_up(g.r, g.tile);
-    g.c_pad = (int32_t)round_up(g.c, g.tile);
+    g.n = (int32_t)kv.second.size();
+    {
+      // 256 x 256 tiles where the group is large enough to fill the machine with them
+      // (and padding to 256 costs little); 128 x 128 otherwise
+      const int64_t t256 = (g.r + kNsLarge - 1) / kNsLarge, c256 = (g.c + kNsLarge - 1) / kNsLarge;
+      const bool big = g.r >= 1024;
+      g.tile_u = big && t256 * c256 * g.n >= 128 ? kNsLarge : kNsSmall;
+      g.tile_g = big && t256 * (t256 + 1) / 2 * g.n >= 192 ? kNsLarge : kNsSmall;
+      g.r_pad = (int32_t)round_up(g.r, std::max(g.tile_g, g.tile_u));
+      g.c_pad = (int32_t)round_up(g.c, g.tile_u);
+    }
     g.n = (int32_t)kv.second.size();
     g.unit_base = (int32_t)p.munits.size();
     const int gi = (int)p.groups.size();
@@ -222,33 +230,30 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
     const Group &g = p.groups[gi];
     p.ns_groups.push_back({(int64_t)g.off_x, (int64_t)g.off_xt0, (int64_t)g.off_xt1, (int64_t)g.off_a,
                            (int64_t)g.off_b, g.r_pad, g.c_pad, g.unit_base, g.n});
-    const int ntr = g.r_pad / kNsTile, ntc = g.c_pad / kNsTile;
+    const int sg = g.tile_g == kNsLarge, su = g.tile_u == kNsLarge;
+    const int ntg = g.r_pad / g.tile_g, ntr = g.r_pad / g.tile_u, ntc = g.c_pad / g.tile_u;
     for (int b = 0; b < g.n; ++b) {
-      for (int tm = 0; tm < ntr; ++tm)
-        for (int tn = tm; tn < ntr; ++tn) {
-          p.ns_gram.push_back({(int32_t)gi, b, tm, tn});
-          p.ns_poly.push_back({(int32_t)gi, b, tm, tn});
+      for (int tm = 0; tm < ntg; ++tm)
+        for (int tn = tm; tn < ntg; ++tn) {
+          p.ns_tiles[0][sg].push_back({(int32_t)gi, b, tm, tn});
+          p.ns_tiles[1][sg].push_back({(int32_t)gi, b, tm, tn});
         }
       for (int tm = 0; tm < ntr; ++tm)
-        for (int tn = 0; tn < ntc; ++tn) p.ns_update.push_back({(int32_t)gi, b, tm, tn});
+        for (int tn = 0; tn < ntc; ++tn) p.ns_tiles[2][su].push_back({(int32_t)gi, b, tm, tn});
     }
   }
-  auto by_k = [&](std::vector<NsTile> &v, bool gram) {
-    std::stable_sort(v.begin(), v.end(), [&](const NsTile &x, const NsTile &y) {
-      const Group &gx = p.groups[x.group], &gy = p.groups[y.group];
-      return (gram ? gx.c_pad : gx.r_pad) > (gram ? gy.c_pad : gy.r_pad);
-    });
-  };
-  by_k(p.ns_gram, true);
-  by_k(p.ns_poly, false);
-  by_k(p.ns_update, false);
-  xcd_order(p.ns_gram, p.groups, true);
-  xcd_order(p.ns_poly, p.groups, false);
-  xcd_order(p.ns_update, p.groups, false);
-  const double t3 = (double)kNsTile * kNsTile * 2.0;
-  for (const NsTile &x : p.ns_gram) p.stats.ns_tile_flops += t3 * p.groups[x.group].c_pad;
-  for (const NsTile &x : p.ns_poly) p.stats.ns_tile_flops += t3 * p.groups[x.group].r_pad;
-  for (const NsTile &x : p.ns_update) p.stats.ns_tile_flops += t3 * p.groups[x.group].r_pad;
+  for (int st = 0; st < 3; ++st)
+    for (int sz = 0; sz < 2; ++sz) {
+      std::vector<NsTile> &v = p.ns_tiles[st][sz];
+      std::stable_sort(v.begin(), v.end(), [&](const NsTile &x, const NsTile &y) {
+        const Group &gx = p.groups[x.group], &gy = p.groups[y.group];
+        return (st == 0 ? gx.c_pad : gx.r_pad) > (st == 0 ? gy.c_pad : gy.r_pad);
+      });
+      xcd_order(v, p.groups, st == 0);
+      const double t = sz ? kNsLarge : kNsSmall;
+      for (const NsTile &x : v)
+        p.stats.ns_tile_flops += t * t * 2.0 * (st == 0 ? p.groups[x.group].c_pad : p.groups[x.group].r_pad);
+    }
   p.stats.ns_tile_flops *= p.opts.ns_steps;
   p.stats.n_muon_units = (int32_t)p.munits.size();
   p.stats.n_groups = (int32_t)p.groups.size();
@@ -350,11 +355,14 @@ size_t table_bytes(const std::vector<T> &v) { return round_up((int64_t)(v.size()
 int upload(sshdp_plan &p) {
   const size_t total = table_bytes(p.munits) + table_bytes(p.f0tiles) + table_bytes(p.aseg_all) +
                        table_bytes(p.aseg_unfused) + table_bytes(p.qregions) + table_bytes(p.qchunks) +
-                       table_bytes(p.ns_groups) + table_bytes(p.ns_gram) + table_bytes(p.ns_poly) +
-                       table_bytes(p.ns_update) + 256;
+                       table_bytes(p.ns_groups) + 256;
+  size_t tiles_total = 0;
+  for (auto &st : p.ns_tiles)
+    for (auto &v : st) tiles_total += table_bytes(v);
   if (hipGetDevice(&p.device) != hipSuccess) return SSHDP_ERR_HIP;
-  if (hipMalloc(&p.dblock, total) != hipSuccess) { p.dblock = nullptr; return SSHDP_ERR_HIP; }
-  std::vector<char> host(total, 0);
+  const size_t all = total + tiles_total;
+  if (hipMalloc(&p.dblock, all) != hipSuccess) { p.dblock = nullptr; return SSHDP_ERR_HIP; }
+  std::vector<char> host(all, 0);
   size_t off = 0;
   auto put = [&](auto &vec, auto *&dptr) {
     using T = typename std::remove_reference<decltype(vec)>::type::value_type;
@@ -369,10 +377,9 @@ int upload(sshdp_plan &p) {
   put(p.qregions, p.d.qregions);
   put(p.qchunks, p.d.qchunks);
   put(p.ns_groups, p.d.ns_groups);
-  put(p.ns_gram, p.d.ns_gram);
-  put(p.ns_poly, p.d.ns_poly);
-  put(p.ns_update, p.d.ns_update);
-  if (hipMemcpy(p.dblock, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) return SSHDP_ERR_HIP;
+  for (int st = 0; st < 3; ++st)
+    for (int sz = 0; sz < 2; ++sz) put(p.ns_tiles[st][sz], p.d.ns_tiles[st][sz]);
+  if (hipMemcpy(p.dblock, host.data(), all, hipMemcpyHostToDevice) != hipSuccess) return SSHDP_ERR_HIP;
   return SSHDP_OK;
 }
 
@@ -460,7 +467,7 @@ int sshdp_plan_group(const sshdp_plan *p, int32_t g, sshdp_group_info *info) {
   if (!p || !info || g < 0 || g >= (int32_t)p->groups.size()) return SSHDP_ERR_ARG;
   const Group &G = p->groups[g];
   info->r = G.r; info->c = G.c; info->r_pad = G.r_pad; info->c_pad = G.c_pad;
-  info->n_units = G.n; info->tile = G.tile;
+  info->n_units = G.n; info->tile = G.tile_u; info->tile_gram = G.tile_g;
   return SSHDP_OK;
 }
 

@@ -108,8 +108,10 @@ def test_planner_groups_and_stats_on_workloads():
         flops = sum(cnt * 5 * (4 * r * r * c + 2 * r ** 3) for (r, c), cnt in shapes.items())
         assert abs(st["ns_flops"] - flops) <= 1e-9 * max(flops, 1)
         for g in p.groups():
-            assert g["r_pad"] % g["tile"] == 0 and g["c_pad"] % g["tile"] == 0
-            assert g["r_pad"] - g["r"] < g["tile"] and g["c_pad"] - g["c"] < g["tile"]
+            t = max(g["tile"], g["tile_gram"])
+            assert g["r_pad"] % t == 0 and g["c_pad"] % g["tile"] == 0
+            assert g["r_pad"] - g["r"] < t and g["c_pad"] - g["c"] < g["tile"]
+            assert g["tile"] in (128, 256) and g["tile_gram"] in (128, 256)
     # the flat shard's requant is fused with AdamW everywhere; the dense block's is not
     wl = workloads.config(4, small=True)
     st = _plan(wl.nodes, wl.root_numel).stats()
