@@ -223,38 +223,90 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[C::MBM][C::MBN]
 }
 
 // f2 on a tile of the last update product: w <- w*decay - lr*scale*x for the
-// elements inside the unit (oriented r x c; a tall unit's view is the transpose).
+// elements inside the unit (oriented r x c; a tall unit's view is the
+// transpose).  The tile goes through LDS in fp32, half its rows at a time,
+// laid out in the view's own orientation, so the read-modify-write of w is
+// 16 contiguous bytes per lane along the view's contiguous dimension.
 template <class C>
 __device__ __forceinline__ void final_tile(const f32x16_t (&acc)[C::MBM][C::MBN], float alpha, float beta,
                                            const uint16_t *DT, int64_t lddt, const MuonUnit &u, float *w, float lr,
-                                           float decay, int r0, int c0, bool zero) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+                                           float decay, int r0, int c0, bool zero, char *smem) {
+  constexpr int HM = C::TM / 2;                      // rows per pass (= one wave row)
+  static_assert(HM == C::WTM, "one pass per wave row");
+  constexpr int PW = C::TN + 4, PT = HM + 4;         // fp32 LDS pitches (wide / tall layout)
+  static_assert(HM * PW * 4 <= C::LDS && C::TN * PT * 4 <= C::LDS, "final tile fits LDS");
+  if (zero && decay == 1.0f) return;                 // direction 0, no decay: w unchanged
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave / C::WN, wn = wave % C::WN;
   const int r_unit = u.tall ? u.cols : u.rows, c_unit = u.tall ? u.rows : u.cols;
   const float ls = lr * u.upd_scale;
+  float *lt = reinterpret_cast<float *>(smem);
 #pragma unroll
-  for (int i = 0; i < C::MBM; ++i) {
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) {
 #pragma unroll
-    for (int j = 0; j < C::MBN; ++j) {
-      const int col = c0 + wn * C::WTN + j * 32 + (lane & 31);
-      if (col >= c_unit) continue;
+      for (int i = 0; i < C::MBM; ++i) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int row0 = r0 + wm * C::WTM + i * 32 + g4 * 8 + (lane >> 5) * 4;
+        for (int j = 0; j < C::MBN; ++j) {
+          const int lc = wn * C::WTN + j * 32 + (lane & 31);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = row0 + q;
-          if (row >= r_unit) continue;
-          float x = 0.f;
-          if (!zero) {
-            x = alpha * acc[i][j][g4 * 4 + q];
-            x = fmaf(beta, bf16_to_f(DT[(int64_t)col * lddt + row]), x);
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int li0 = i * 32 + g4 * 8 + (lane >> 5) * 4;       // row within the pass
+            float x[4] = {0.f, 0.f, 0.f, 0.f};
+            if (!zero) {
+              const uint2 d = *reinterpret_cast<const uint2 *>(DT + (int64_t)(c0 + lc) * lddt + r0 + h * HM + li0);
+              x[0] = fmaf(beta, __uint_as_float(d.x << 16), alpha * acc[i][j][g4 * 4 + 0]);
+              x[1] = fmaf(beta, __uint_as_float(d.x & 0xFFFF0000u), alpha * acc[i][j][g4 * 4 + 1]);
+              x[2] = fmaf(beta, __uint_as_float(d.y << 16), alpha * acc[i][j][g4 * 4 + 2]);
+              x[3] = fmaf(beta, __uint_as_float(d.y & 0xFFFF0000u), alpha * acc[i][j][g4 * 4 + 3]);
+            }
+            if (u.tall) {
+              *reinterpret_cast<float4 *>(&lt[lc * PT + li0]) = make_float4(x[0], x[1], x[2], x[3]);
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) lt[(li0 + q) * PW + lc] = x[q];
+            }
           }
-          const int64_t idx = u.tall ? u.abs + (int64_t)col * u.row_stride + row
-                                     : u.abs + (int64_t)row * u.row_stride + col;
-          w[idx] = fmaf(w[idx], decay, -ls * x);
         }
       }
     }
+    __syncthreads();
+    const int rb = r0 + h * HM;                      // first oriented row of this pass
+    if (!u.tall) {
+      // view row i = oriented row, contiguous along oriented columns
+      constexpr int CH = C::TN / 4;
+      for (int id = t; id < HM * CH; id += C::NT) {
+        const int li = id / CH, j4 = (id - li * CH) * 4;
+        const int row = rb + li, col = c0 + j4;
+        if (row < r_unit && col < c_unit) {
+          float4 *pw = reinterpret_cast<float4 *>(w + u.abs + (int64_t)row * u.row_stride + col);
+          const float4 xv = *reinterpret_cast<const float4 *>(&lt[li * PW + j4]);
+          float4 wv = *pw;
+          wv.x = fmaf(wv.x, decay, -ls * xv.x);
+          wv.y = fmaf(wv.y, decay, -ls * xv.y);
+          wv.z = fmaf(wv.z, decay, -ls * xv.z);
+          wv.w = fmaf(wv.w, decay, -ls * xv.w);
+          *pw = wv;
+        }
+      }
+    } else {
+      // view row = oriented column, contiguous along oriented rows
+      constexpr int CH = HM / 4;
+      for (int id = t; id < C::TN * CH; id += C::NT) {
+        const int lc = id / CH, i4 = (id - lc * CH) * 4;
+        const int row = rb + i4, col = c0 + lc;
+        if (row < r_unit && col < c_unit) {
+          float4 *pw = reinterpret_cast<float4 *>(w + u.abs + (int64_t)col * u.row_stride + row);
+          const float4 xv = *reinterpret_cast<const float4 *>(&lt[lc * PT + i4]);
+          float4 wv = *pw;
+          wv.x = fmaf(wv.x, decay, -ls * xv.x);
+          wv.y = fmaf(wv.y, decay, -ls * xv.y);
+          wv.z = fmaf(wv.z, decay, -ls * xv.z);
+          wv.w = fmaf(wv.w, decay, -ls * xv.w);
+          *pw = wv;
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -314,7 +366,7 @@ __global__ __launch_bounds__(C::NT, C::NT == 256 ? 2 : 1) void k_ns(NsArgs a) {
         gemm_core<C>(reinterpret_cast<const char *>(B + r0 * rp), reinterpret_cast<const char *>(XTc + c0 * rp),
                         rp, smem, acc);
       const MuonUnit u = a.units[unit];
-      final_tile<C>(acc, al, be, XTc, rp, u, a.w, a.lr, a.decay, r0, c0, zero);
+      final_tile<C>(acc, al, be, XTc, rp, u, a.w, a.lr, a.decay, r0, c0, zero, smem);
     }
   }
 }
