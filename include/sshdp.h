@@ -32,10 +32,14 @@
  * caller-owned, must stay valid until the enqueued work has run, and must be
  * 16-byte aligned.  `stream` is a hipStream_t passed as void* (NULL = the
  * default stream); every launching call is asynchronous on it, performs no
- * allocation and no synchronisation.  Plans are immutable after creation; calls
- * on different streams with different workspaces may overlap, calls sharing a
- * workspace are serialised by the caller's stream order.  The library keeps no
- * state between calls: the step counter is an argument.
+ * allocation and no synchronisation.  Newton-Schulz groups of one call may run
+ * on up to three plan-owned side streams (default priority) that are forked
+ * from and joined back into `stream` with events, so the call behaves as one
+ * ordered unit of work on `stream` (and can be captured into a HIP graph).
+ * Calls with one plan use its side streams: issue them from one host thread,
+ * in order (their work is then ordered as issued).  Calls sharing a workspace
+ * are serialised by the caller's stream order.  The library keeps no state
+ * between calls: the step counter is an argument.
  */
 #ifndef SSHDP_H
 #define SSHDP_H
@@ -236,9 +240,11 @@ int sshdp_gemm_bf16_nt(const void *P, const void *Q, const void *D, void *O, voi
  * calls bracket each kernel class with HIP events on the launch stream and
  * accumulate durations (milliseconds) and launch counts; reading synchronises
  * on those events.  Classes: 0 momentum (f0), 1 norm, 2 NS Gram, 3 NS poly,
- * 4 NS update (+f2), 5 AdamW, 6 AdamW+G fused, 7 G requant.  Not thread-safe;
- * for measurement only. */
-enum { SSHDP_PROF_CLASSES = 8 };
+ * 4 NS update (+f2), 5 AdamW, 6 AdamW+G fused, 7 G requant, 8 the whole
+ * Newton-Schulz phase on the caller's stream (fork to join: NS launches of
+ * different groups run concurrently on plan-owned streams, so classes 2-4 can
+ * overlap in time).  Not thread-safe; for measurement only. */
+enum { SSHDP_PROF_CLASSES = 9 };
 int sshdp_profile_enable(sshdp_plan *plan, int32_t enable);
 int sshdp_profile_read(sshdp_plan *plan, double *ms, int64_t *launches);
 

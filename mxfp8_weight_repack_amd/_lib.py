@@ -22,7 +22,8 @@ ERROR_NAMES = {ERR_ARG: "ARG", ERR_TREE: "TREE", ERR_BOUNDS: "BOUNDS", ERR_OVERL
 OPT = {None: 0, "muon": 1, "adamw": 2}
 LAYOUT = {"rowmajor": 0, "tile32x4": 1}
 PLAN_HOST_ONLY = 1
-PROF_CLASSES = ["momentum", "norm", "ns_gram", "ns_poly", "ns_update", "adamw", "adamw_requant", "requant"]
+PROF_CLASSES = ["momentum", "norm", "ns_gram", "ns_poly", "ns_update", "adamw", "adamw_requant", "requant",
+                "ns_phase"]
 
 
 class SshdpError(RuntimeError):

@@ -75,23 +75,31 @@ int run_muon(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_muon_hp *h
     e = launch_norm(*p, w, p->opts.ns_eps, s);
   }
   if (e != hipSuccess) return SSHDP_ERR_HIP;
+  // Newton-Schulz: lane 0 on the caller's stream, the other lanes on plan-owned
+  // streams forked from and joined back into it by events
+  Prof wall(p, 8, s);
+  if (p->n_lanes > 1) {
+    if (hipEventRecord(p->ev_fork, s) != hipSuccess) return SSHDP_ERR_HIP;
+    for (int ln = 1; ln < p->n_lanes; ++ln)
+      if (hipStreamWaitEvent(p->lane_stream[ln], p->ev_fork, 0) != hipSuccess) return SSHDP_ERR_HIP;
+  }
   const int steps = p->opts.ns_steps;
   for (int it = 0; it < steps; ++it) {
-    {
-      Prof pr(p, 2, s);
-      e = launch_ns_stage(*p, 0, it, w, b->w_main, hp->lr, hp->weight_decay, s);
+    for (int stage = 0; stage < 3; ++stage) {
+      const int kind = stage < 2 ? stage : (it + 1 == steps ? 3 : 2);
+      for (int ln = 0; ln < p->n_lanes; ++ln) {
+        hipStream_t ls = ln == 0 ? s : p->lane_stream[ln];
+        Prof pr(p, 2 + stage, ls);
+        e = launch_ns_stage(*p, ln, kind, it, w, b->w_main, hp->lr, hp->weight_decay, ls);
+        if (e != hipSuccess) return SSHDP_ERR_HIP;
+      }
     }
-    if (e != hipSuccess) return SSHDP_ERR_HIP;
-    {
-      Prof pr(p, 3, s);
-      e = launch_ns_stage(*p, 1, it, w, b->w_main, hp->lr, hp->weight_decay, s);
+  }
+  if (p->n_lanes > 1) {
+    for (int ln = 1; ln < p->n_lanes; ++ln) {
+      if (hipEventRecord(p->ev_join[ln], p->lane_stream[ln]) != hipSuccess) return SSHDP_ERR_HIP;
+      if (hipStreamWaitEvent(s, p->ev_join[ln], 0) != hipSuccess) return SSHDP_ERR_HIP;
     }
-    if (e != hipSuccess) return SSHDP_ERR_HIP;
-    {
-      Prof pr(p, 4, s);
-      e = launch_ns_stage(*p, it + 1 == steps ? 3 : 2, it, w, b->w_main, hp->lr, hp->weight_decay, s);
-    }
-    if (e != hipSuccess) return SSHDP_ERR_HIP;
   }
   return SSHDP_OK;
 }

@@ -14,6 +14,7 @@ namespace sshdp {
 constexpr int kF0Tile = 64;          // f0 transposing tile edge (elements)
 constexpr int kNsSmall = 128;        // Newton-Schulz GEMM macro tiles: 128 x 128 (4 waves) ...
 constexpr int kNsLarge = 256;        // ... or 256 x 256 (8 waves), chosen per group and stage
+constexpr int kMaxLanes = 4;         // Newton-Schulz groups run on up to 4 concurrent streams
 constexpr int kChunk = 4096;         // elements per AdamW / requant work item
 constexpr size_t kAlign = 256;       // workspace sub-buffer alignment (bytes)
 
@@ -91,7 +92,7 @@ struct DeviceTables {
   QRegion *qregions = nullptr;
   QChunk *qchunks = nullptr;
   NsGroupDev *ns_groups = nullptr;
-  NsTile *ns_tiles[3][2] = {};   // [stage: Gram, poly, update][tile: 128, 256]
+  NsTile *ns_tiles[kMaxLanes][3][2] = {};   // [lane][stage: Gram, poly, update][tile: 128, 256]
 };
 
 }  // namespace sshdp
@@ -105,7 +106,13 @@ struct sshdp_plan {
   std::vector<sshdp::F0Tile> f0tiles;
   std::vector<sshdp::Group> groups;
   std::vector<sshdp::NsGroupDev> ns_groups;
-  std::vector<sshdp::NsTile> ns_tiles[3][2];   // per stage and tile size, longest K first
+  // Newton-Schulz groups are dealt to lanes (lane 0 = the caller's stream, others = plan-owned
+  // streams joined back by events); per lane, stage and tile size a tile table, longest K first
+  int n_lanes = 1;
+  std::vector<int32_t> group_lane;
+  std::vector<sshdp::NsTile> ns_tiles[sshdp::kMaxLanes][3][2];
+  hipStream_t lane_stream[sshdp::kMaxLanes] = {};
+  hipEvent_t ev_fork = nullptr, ev_join[sshdp::kMaxLanes] = {};
   std::vector<sshdp::ASeg> aseg_all, aseg_unfused;
   std::vector<sshdp::QRegion> qregions;
   std::vector<sshdp::QChunk> qchunks;   // fused-eligible chunks first
@@ -130,8 +137,8 @@ hipError_t launch_f0(const sshdp_plan &p, const float *g, float *m, float mu, in
                      hipStream_t s);
 hipError_t launch_norm(const sshdp_plan &p, char *ws, float eps, hipStream_t s);
 // stage: 0 Gram, 1 poly, 2 update, 3 final update (+f2); one launch covers all groups
-hipError_t launch_ns_stage(const sshdp_plan &p, int stage, int iter, char *ws, float *w_main, float lr, float wd,
-                           hipStream_t s);
+hipError_t launch_ns_stage(const sshdp_plan &p, int lane, int stage, int iter, char *ws, float *w_main, float lr,
+                           float wd, hipStream_t s);
 hipError_t launch_gemm_raw(const void *P, const void *Q, const void *D, void *O, void *OT, int M, int N,
                            int K, int batch, float alpha, float beta, int tile, hipStream_t s);
 hipError_t launch_adamw(const ASeg *segs, int64_t nseg, const sshdp_buffers &b, const sshdp_adamw_hp &hp,

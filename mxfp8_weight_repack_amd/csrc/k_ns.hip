@@ -404,24 +404,24 @@ hipError_t launch_list(const NsArgs &a, size_t n, hipStream_t s) {
 }
 
 template <int STAGE>
-hipError_t launch_sizes(const sshdp_plan &p, NsArgs a, int st, hipStream_t s) {
+hipError_t launch_sizes(const sshdp_plan &p, NsArgs a, int ln, int st, hipStream_t s) {
   hipError_t e = hipSuccess;
-  if (!p.ns_tiles[st][1].empty()) {           // 256-tile work first: it is the long part
-    a.tiles = p.d.ns_tiles[st][1];
-    e = launch_list<STAGE, CLarge>(a, p.ns_tiles[st][1].size(), s);
+  if (!p.ns_tiles[ln][st][1].empty()) {       // 256-tile work first: it is the long part
+    a.tiles = p.d.ns_tiles[ln][st][1];
+    e = launch_list<STAGE, CLarge>(a, p.ns_tiles[ln][st][1].size(), s);
     if (e != hipSuccess) return e;
   }
-  if (!p.ns_tiles[st][0].empty()) {
-    a.tiles = p.d.ns_tiles[st][0];
-    e = launch_list<STAGE, CSmall>(a, p.ns_tiles[st][0].size(), s);
+  if (!p.ns_tiles[ln][st][0].empty()) {
+    a.tiles = p.d.ns_tiles[ln][st][0];
+    e = launch_list<STAGE, CSmall>(a, p.ns_tiles[ln][st][0].size(), s);
   }
   return e;
 }
 
 }  // namespace
 
-hipError_t launch_ns_stage(const sshdp_plan &p, int stage, int iter, char *ws, float *w_main, float lr, float wd,
-                           hipStream_t s) {
+hipError_t launch_ns_stage(const sshdp_plan &p, int lane, int stage, int iter, char *ws, float *w_main, float lr,
+                           float wd, hipStream_t s) {
   NsArgs a{};
   a.ws = ws;
   a.groups = p.d.ns_groups;
@@ -435,10 +435,10 @@ hipError_t launch_ns_stage(const sshdp_plan &p, int stage, int iter, char *ws, f
   a.cc = p.opts.ns_c;
   a.iter = iter;
   switch (stage) {
-    case 0: return launch_sizes<0>(p, a, 0, s);
-    case 1: return launch_sizes<1>(p, a, 1, s);
-    case 2: return launch_sizes<2>(p, a, 2, s);
-    default: return launch_sizes<3>(p, a, 2, s);
+    case 0: return launch_sizes<0>(p, a, lane, 0, s);
+    case 1: return launch_sizes<1>(p, a, lane, 1, s);
+    case 2: return launch_sizes<2>(p, a, lane, 2, s);
+    default: return launch_sizes<3>(p, a, lane, 2, s);
   }
 }
 

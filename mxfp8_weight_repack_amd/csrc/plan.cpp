@@ -225,35 +225,60 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
     }
   }
   p.ws_bytes = off;
-  // per-stage tile tables: symmetric Gram/poly take tm <= tn; longest K first
+  // per-group cost (executed MFMA flops per step), groups dealt to lanes largest first
+  std::vector<double> cost(p.groups.size(), 0.0);
+  for (size_t gi = 0; gi < p.groups.size(); ++gi) {
+    const Group &g = p.groups[gi];
+    const double tg = g.tile_g, tu = g.tile_u;
+    const double ntg = g.r_pad / g.tile_g, ntr = g.r_pad / g.tile_u, ntc = g.c_pad / g.tile_u;
+    cost[gi] = g.n * (ntg * (ntg + 1) / 2 * tg * tg * 2.0 * (g.c_pad + g.r_pad) + ntr * ntc * tu * tu * 2.0 * g.r_pad);
+  }
+  std::vector<size_t> order(p.groups.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) { return cost[x] > cost[y]; });
+  p.n_lanes = (int)std::min<size_t>(std::max<size_t>(p.groups.size(), 1), kMaxLanes);
+  p.group_lane.assign(p.groups.size(), 0);
+  {
+    std::vector<double> load(p.n_lanes, 0.0);
+    for (size_t k = 0; k < order.size(); ++k) {
+      int best = 0;
+      for (int l = 1; l < p.n_lanes; ++l)
+        if (load[l] < load[best]) best = l;
+      p.group_lane[order[k]] = best;
+      load[best] += cost[order[k]];
+    }
+  }
+  // per-lane, per-stage tile tables: symmetric Gram/poly take tm <= tn; longest K first
   for (size_t gi = 0; gi < p.groups.size(); ++gi) {
     const Group &g = p.groups[gi];
     p.ns_groups.push_back({(int64_t)g.off_x, (int64_t)g.off_xt0, (int64_t)g.off_xt1, (int64_t)g.off_a,
                            (int64_t)g.off_b, g.r_pad, g.c_pad, g.unit_base, g.n});
+    const int ln = p.group_lane[gi];
     const int sg = g.tile_g == kNsLarge, su = g.tile_u == kNsLarge;
     const int ntg = g.r_pad / g.tile_g, ntr = g.r_pad / g.tile_u, ntc = g.c_pad / g.tile_u;
     for (int b = 0; b < g.n; ++b) {
       for (int tm = 0; tm < ntg; ++tm)
         for (int tn = tm; tn < ntg; ++tn) {
-          p.ns_tiles[0][sg].push_back({(int32_t)gi, b, tm, tn});
-          p.ns_tiles[1][sg].push_back({(int32_t)gi, b, tm, tn});
+          p.ns_tiles[ln][0][sg].push_back({(int32_t)gi, b, tm, tn});
+          p.ns_tiles[ln][1][sg].push_back({(int32_t)gi, b, tm, tn});
         }
       for (int tm = 0; tm < ntr; ++tm)
-        for (int tn = 0; tn < ntc; ++tn) p.ns_tiles[2][su].push_back({(int32_t)gi, b, tm, tn});
+        for (int tn = 0; tn < ntc; ++tn) p.ns_tiles[ln][2][su].push_back({(int32_t)gi, b, tm, tn});
     }
   }
-  for (int st = 0; st < 3; ++st)
-    for (int sz = 0; sz < 2; ++sz) {
-      std::vector<NsTile> &v = p.ns_tiles[st][sz];
-      std::stable_sort(v.begin(), v.end(), [&](const NsTile &x, const NsTile &y) {
-        const Group &gx = p.groups[x.group], &gy = p.groups[y.group];
-        return (st == 0 ? gx.c_pad : gx.r_pad) > (st == 0 ? gy.c_pad : gy.r_pad);
-      });
-      xcd_order(v, p.groups, st == 0);
-      const double t = sz ? kNsLarge : kNsSmall;
-      for (const NsTile &x : v)
-        p.stats.ns_tile_flops += t * t * 2.0 * (st == 0 ? p.groups[x.group].c_pad : p.groups[x.group].r_pad);
-    }
+  for (int ln = 0; ln < p.n_lanes; ++ln)
+    for (int st = 0; st < 3; ++st)
+      for (int sz = 0; sz < 2; ++sz) {
+        std::vector<NsTile> &v = p.ns_tiles[ln][st][sz];
+        std::stable_sort(v.begin(), v.end(), [&](const NsTile &x, const NsTile &y) {
+          const Group &gx = p.groups[x.group], &gy = p.groups[y.group];
+          return (st == 0 ? gx.c_pad : gx.r_pad) > (st == 0 ? gy.c_pad : gy.r_pad);
+        });
+        xcd_order(v, p.groups, st == 0);
+        const double t = sz ? kNsLarge : kNsSmall;
+        for (const NsTile &x : v)
+          p.stats.ns_tile_flops += t * t * 2.0 * (st == 0 ? p.groups[x.group].c_pad : p.groups[x.group].r_pad);
+      }
   p.stats.ns_tile_flops *= p.opts.ns_steps;
   p.stats.n_muon_units = (int32_t)p.munits.size();
   p.stats.n_groups = (int32_t)p.groups.size();
@@ -357,8 +382,9 @@ int upload(sshdp_plan &p) {
                        table_bytes(p.aseg_unfused) + table_bytes(p.qregions) + table_bytes(p.qchunks) +
                        table_bytes(p.ns_groups) + 256;
   size_t tiles_total = 0;
-  for (auto &st : p.ns_tiles)
-    for (auto &v : st) tiles_total += table_bytes(v);
+  for (auto &ln : p.ns_tiles)
+    for (auto &st : ln)
+      for (auto &v : st) tiles_total += table_bytes(v);
   if (hipGetDevice(&p.device) != hipSuccess) return SSHDP_ERR_HIP;
   const size_t all = total + tiles_total;
   if (hipMalloc(&p.dblock, all) != hipSuccess) { p.dblock = nullptr; return SSHDP_ERR_HIP; }
@@ -377,9 +403,18 @@ int upload(sshdp_plan &p) {
   put(p.qregions, p.d.qregions);
   put(p.qchunks, p.d.qchunks);
   put(p.ns_groups, p.d.ns_groups);
-  for (int st = 0; st < 3; ++st)
-    for (int sz = 0; sz < 2; ++sz) put(p.ns_tiles[st][sz], p.d.ns_tiles[st][sz]);
+  for (int ln = 0; ln < kMaxLanes; ++ln)
+    for (int st = 0; st < 3; ++st)
+      for (int sz = 0; sz < 2; ++sz) put(p.ns_tiles[ln][st][sz], p.d.ns_tiles[ln][st][sz]);
   if (hipMemcpy(p.dblock, host.data(), all, hipMemcpyHostToDevice) != hipSuccess) return SSHDP_ERR_HIP;
+  // side streams (default priority, non-blocking) and the events that fork/join them
+  if (p.n_lanes > 1) {
+    if (hipEventCreateWithFlags(&p.ev_fork, hipEventDisableTiming) != hipSuccess) return SSHDP_ERR_HIP;
+    for (int ln = 1; ln < p.n_lanes; ++ln) {
+      if (hipStreamCreateWithFlags(&p.lane_stream[ln], hipStreamNonBlocking) != hipSuccess) return SSHDP_ERR_HIP;
+      if (hipEventCreateWithFlags(&p.ev_join[ln], hipEventDisableTiming) != hipSuccess) return SSHDP_ERR_HIP;
+    }
+  }
   return SSHDP_OK;
 }
 
@@ -487,6 +522,11 @@ void sshdp_plan_destroy(sshdp_plan *p) {
     (void)hipFree(p->dblock);
     if (cur >= 0 && cur != p->device) (void)hipSetDevice(cur);
   }
+  for (int ln = 1; ln < kMaxLanes; ++ln) {
+    if (p->lane_stream[ln]) (void)hipStreamDestroy(p->lane_stream[ln]);
+    if (p->ev_join[ln]) (void)hipEventDestroy(p->ev_join[ln]);
+  }
+  if (p->ev_fork) (void)hipEventDestroy(p->ev_fork);
   for (auto &e : p->prof_pending) { (void)hipEventDestroy(e.second.first); (void)hipEventDestroy(e.second.second); }
   for (hipEvent_t e : p->prof_pool) (void)hipEventDestroy(e);
   delete p;
