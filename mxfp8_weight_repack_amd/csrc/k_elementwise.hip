@@ -26,6 +26,14 @@ namespace {
 
 __device__ __forceinline__ uint32_t fbits(float x) { return __float_as_uint(x); }
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// streaming load that is not kept in the caches (read-once data)
+__device__ __forceinline__ float4 load_nt(const float *p) {
+  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 // ----------------------------------------------------------------------------- f0
 // One 64x64 tile of a Muon unit's own (padded) layout per workgroup of 256.
 // Elements outside the unit write u = 0 (the padding the GEMMs rely on).
@@ -116,17 +124,21 @@ __global__ __launch_bounds__(256) void k_norm(const MuonUnit *__restrict__ units
 
 // ----------------------------------------------------------------------------- AdamW
 struct AdamConst {
-  float lr, b1, b2, eps, decay;   // decay = 1 - lr*wd
-  float omb1, omb2, bc1, bc2;     // 1-b1, 1-b2, 1-b1^t, 1-b2^t
+  float b1, b2, eps, decay;       // decay = 1 - lr*wd
+  float omb1, omb2;               // 1-b1, 1-b2
+  float lr_bc1, rbc2;             // lr/(1-b1^t), 1/(1-b2^t)  (bias corrections folded, host fp64)
 };
 
+// w <- w*decay; m <- b1 m + (1-b1) g; v <- b2 v + (1-b2) g^2;
+// w <- w - (lr/(1-b1^t)) m / (sqrt(v/(1-b2^t)) + eps).  The square root and the
+// reciprocal are the hardware's (within 1 ulp): the streaming pass stays
+// memory-bound instead of spending ~40 ALU ops per element on IEEE division.
 __device__ __forceinline__ void adam_elem(float &w, float g, float &m, float &v, const AdamConst &c) {
   w = w * c.decay;
   m = fmaf(c.b1, m, c.omb1 * g);
   v = fmaf(c.b2, v, c.omb2 * (g * g));
-  const float mhat = m / c.bc1;
-  const float vhat = v / c.bc2;
-  w = w - c.lr * (mhat / (sqrtf(vhat) + c.eps));
+  const float den = __builtin_amdgcn_sqrtf(v * c.rbc2) + c.eps;
+  w = fmaf(-c.lr_bc1, m * __builtin_amdgcn_rcpf(den), w);
 }
 
 __global__ __launch_bounds__(256) void k_adamw(const ASeg *__restrict__ segs, float *__restrict__ w,
@@ -170,6 +182,54 @@ __global__ __launch_bounds__(256) void k_adamw(const ASeg *__restrict__ segs, fl
 // One chunk (<= kChunk elements, whole 32-blocks) per workgroup; four passes of
 // 1024 elements, each lane owning 4 consecutive elements, 8 lanes per block.
 // All loads of a chunk are issued before any arithmetic.
+// Quantise 4 elements per lane (8 lanes = one 32-element block) and store
+// their codes and the block's scale byte.  All 64 lanes must call it (the
+// block amax is a butterfly over lane groups of 8); `live` masks the stores.
+__device__ __forceinline__ void quant_store(const float4 &wv, int64_t e, bool live, int t, const QChunk &q,
+                                            const QRegion *__restrict__ regions, int tile_layout,
+                                            uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+  // block amax over 8 lanes (an integer max of |x| bits also ranks NaN > Inf)
+  const uint32_t b0 = fbits(wv.x), b1 = fbits(wv.y), b2 = fbits(wv.z), b3 = fbits(wv.w);
+  uint32_t a = max(max(b0 & 0x7FFFFFFFu, b1 & 0x7FFFFFFFu), max(b2 & 0x7FFFFFFFu, b3 & 0x7FFFFFFFu));
+  a = max(a, (uint32_t)__shfl_xor((int)a, 1));
+  a = max(a, (uint32_t)__shfl_xor((int)a, 2));
+  a = max(a, (uint32_t)__shfl_xor((int)a, 4));
+  if (!live) return;
+  const uint32_t sb = mx_scale_byte(a);
+  uint32_t packed;
+  if (sb == 0xFFu) {
+    packed = 0x7F7F7F7Fu;
+  } else {
+    // y = x * 2^-e is exact down to 2^-126 (and anything smaller encodes as a
+    // signed zero either way); gfx950's packed fp8 convert is OCP E4M3FN with
+    // round-to-nearest-even, bit-identical to mx_e4m3_code for every finite
+    // |y| <= 448 (checked exhaustively on the device)
+    const int ex = 127 - (int)sb;
+    const float y0 = ldexpf(wv.x, ex), y1 = ldexpf(wv.y, ex), y2 = ldexpf(wv.z, ex), y3 = ldexpf(wv.w, ex);
+    int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+    pk = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, pk, true);
+    packed = (uint32_t)pk;
+  }
+  __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t *>(codes + e));
+  if ((t & 7) == 0) {
+    int64_t idx = e >> 5;
+    if (tile_layout) {
+      const QRegion r = regions[q.region];
+      const int64_t rel = e - r.abs;
+      const int64_t n = rel / r.cols;
+      const int64_t kb = (rel - n * r.cols) >> 5;
+      const int64_t KB = r.cols >> 5;
+      idx = (r.abs >> 5) + ((n >> 5) * (KB >> 2) + (kb >> 2)) * 128 + (n & 31) * 4 + (kb & 3);
+    }
+    scales[idx] = (uint8_t)sb;
+  }
+}
+
+// One chunk (<= kChunk elements, whole 32-blocks) per workgroup; four passes of
+// 1024 elements, each lane owning 4 consecutive elements, 8 lanes per block.
+// All loads of a chunk are issued before any arithmetic.  A chunk that is full
+// and (when fused) wholly AdamW-updated takes a branch-free path; the others
+// (region tails, runs that start or end inside the chunk) mask per element.
 template <bool FUSED>
 __global__ __launch_bounds__(256) void k_quant(const QChunk *__restrict__ chunks, const QRegion *__restrict__ regions,
                                                int tile_layout, float *__restrict__ w, const float *__restrict__ g,
@@ -180,6 +240,34 @@ __global__ __launch_bounds__(256) void k_quant(const QChunk *__restrict__ chunks
   const QChunk q = chunks[blockIdx.x];
   const int t = threadIdx.x;
   float4 wv[P], gv[P], mv[P], vv[P];
+  const bool full = q.n == kChunk && (!FUSED || (q.lo <= q.base && q.hi >= q.base + kChunk));
+  if (full) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int64_t e = q.base + p * 1024 + 4 * t;
+      wv[p] = *reinterpret_cast<const float4 *>(w + e);
+      if (FUSED) {
+        gv[p] = load_nt(g + e);
+        mv[p] = *reinterpret_cast<const float4 *>(m + e);
+        vv[p] = *reinterpret_cast<const float4 *>(v + e);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int64_t e = q.base + p * 1024 + 4 * t;
+      if (FUSED) {
+        adam_elem(wv[p].x, gv[p].x, mv[p].x, vv[p].x, c);
+        adam_elem(wv[p].y, gv[p].y, mv[p].y, vv[p].y, c);
+        adam_elem(wv[p].z, gv[p].z, mv[p].z, vv[p].z, c);
+        adam_elem(wv[p].w, gv[p].w, mv[p].w, vv[p].w, c);
+        *reinterpret_cast<float4 *>(w + e) = wv[p];
+        *reinterpret_cast<float4 *>(m + e) = mv[p];
+        *reinterpret_cast<float4 *>(v + e) = vv[p];
+      }
+      quant_store(wv[p], e, true, t, q, regions, tile_layout, codes, scales);
+    }
+    return;
+  }
   bool live[P], upd[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) wv[p] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -191,7 +279,7 @@ __global__ __launch_bounds__(256) void k_quant(const QChunk *__restrict__ chunks
     upd[p] = FUSED && live[p] && e + 4 > q.lo && e < q.hi;
     if (live[p]) wv[p] = *reinterpret_cast<const float4 *>(w + e);
     if (upd[p]) {
-      gv[p] = *reinterpret_cast<const float4 *>(g + e);
+      gv[p] = load_nt(g + e);
       mv[p] = *reinterpret_cast<const float4 *>(m + e);
       vv[p] = *reinterpret_cast<const float4 *>(v + e);
     }
@@ -204,67 +292,30 @@ __global__ __launch_bounds__(256) void k_quant(const QChunk *__restrict__ chunks
       const float *gp = reinterpret_cast<const float *>(&gv[p]);
       float *mp = reinterpret_cast<float *>(&mv[p]);
       float *vp = reinterpret_cast<float *>(&vv[p]);
-      if (e >= q.lo && e + 4 <= q.hi) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) adam_elem(wp[j], gp[j], mp[j], vp[j], c);
-        *reinterpret_cast<float4 *>(w + e) = wv[p];
-        *reinterpret_cast<float4 *>(m + e) = mv[p];
-        *reinterpret_cast<float4 *>(v + e) = vv[p];
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (e + j >= q.lo && e + j < q.hi) {
-            adam_elem(wp[j], gp[j], mp[j], vp[j], c);
-            w[e + j] = wp[j];
-            m[e + j] = mp[j];
-            v[e + j] = vp[j];
-          }
+      for (int j = 0; j < 4; ++j) {
+        if (e + j >= q.lo && e + j < q.hi) {
+          adam_elem(wp[j], gp[j], mp[j], vp[j], c);
+          w[e + j] = wp[j];
+          m[e + j] = mp[j];
+          v[e + j] = vp[j];
         }
       }
     }
-    // block amax over 8 lanes (an integer max of |x| bits also ranks NaN > Inf)
-    const uint32_t b0 = fbits(wv[p].x), b1 = fbits(wv[p].y), b2 = fbits(wv[p].z), b3 = fbits(wv[p].w);
-    uint32_t a = max(max(b0 & 0x7FFFFFFFu, b1 & 0x7FFFFFFFu), max(b2 & 0x7FFFFFFFu, b3 & 0x7FFFFFFFu));
-    a = max(a, (uint32_t)__shfl_xor((int)a, 1));
-    a = max(a, (uint32_t)__shfl_xor((int)a, 2));
-    a = max(a, (uint32_t)__shfl_xor((int)a, 4));
-    if (!live[p]) continue;
-    const uint32_t sb = mx_scale_byte(a);
-    uint32_t packed;
-    if (sb == 0xFFu) {
-      packed = 0x7F7F7F7Fu;
-    } else {
-      const int ex = (int)sb - 127;
-      packed = mx_e4m3_code(b0, ex) | (mx_e4m3_code(b1, ex) << 8) | (mx_e4m3_code(b2, ex) << 16) |
-               (mx_e4m3_code(b3, ex) << 24);
-    }
-    *reinterpret_cast<uint32_t *>(codes + e) = packed;
-    if ((t & 7) == 0) {
-      int64_t idx = e >> 5;
-      if (tile_layout) {
-        const QRegion r = regions[q.region];
-        const int64_t rel = e - r.abs;
-        const int64_t n = rel / r.cols;
-        const int64_t kb = (rel - n * r.cols) >> 5;
-        const int64_t KB = r.cols >> 5;
-        idx = (r.abs >> 5) + ((n >> 5) * (KB >> 2) + (kb >> 2)) * 128 + (n & 31) * 4 + (kb & 3);
-      }
-      scales[idx] = (uint8_t)sb;
-    }
+    quant_store(wv[p], e, live[p], t, q, regions, tile_layout, codes, scales);
   }
 }
 
 AdamConst adam_const(const sshdp_adamw_hp &hp, int64_t step) {
   AdamConst c;
-  c.lr = hp.lr;
   c.b1 = hp.beta1;
   c.b2 = hp.beta2;
   c.eps = hp.eps;
   c.decay = (float)(1.0 - (double)hp.lr * (double)hp.weight_decay);
   c.omb1 = (float)(1.0 - (double)hp.beta1);
   c.omb2 = (float)(1.0 - (double)hp.beta2);
-  c.bc1 = (float)(1.0 - std::pow((double)hp.beta1, (double)step));
-  c.bc2 = (float)(1.0 - std::pow((double)hp.beta2, (double)step));
+  c.lr_bc1 = (float)((double)hp.lr / (1.0 - std::pow((double)hp.beta1, (double)step)));
+  c.rbc2 = (float)(1.0 / (1.0 - std::pow((double)hp.beta2, (double)step)));
   return c;
 }
 

@@ -34,17 +34,20 @@ MX_HD uint32_t mx_scale_byte(uint32_t amax_bits) {
   return (uint32_t)(e + 127);
 }
 
-// Round-to-nearest-even right shift of a 24-bit significand (sh may be <= 0).
+// Round-to-nearest-even right shift of a significand m < 2^24 by sh bits
+// (sh <= 0 shifts left, at most by 3 here).  Written with selects only, so a
+// wavefront runs it without divergent branches.
 MX_HD uint32_t mx_rne_shr(uint32_t m, int sh) {
-  if (sh <= 0) return m << (-sh);
-  if (sh > 25) return 0u;
-  const uint32_t q = m >> sh;
-  const uint32_t rem = m & ((1u << sh) - 1u);
-  const uint32_t half = 1u << (sh - 1);
-  return q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u);
+  const int s = sh < 0 ? 0 : (sh > 31 ? 31 : sh);
+  const uint32_t q = m >> s;
+  const uint32_t rem = m & ((1u << s) - 1u);
+  const uint32_t half = s > 0 ? 1u << (s - 1) : 0u;
+  const uint32_t up = (rem > half || (rem == half && half != 0u && (q & 1u))) ? 1u : 0u;
+  const uint32_t left = m << (sh < 0 ? -sh : 0);
+  return sh <= 0 ? left : q + up;
 }
 
-MX_HD int mx_clz32(uint32_t v) {
+MX_HD int mx_clz32(uint32_t v) {                     // v != 0
 #if defined(__HIPCC__) || defined(__GNUC__)
   return __builtin_clz(v);
 #else
@@ -56,22 +59,23 @@ MX_HD int mx_clz32(uint32_t v) {
 
 // E4M3FN code of x * 2^-e for a finite float32 x (bits) whose block has scale
 // exponent e (so |x * 2^-e| <= 448).  Ties to the even mantissa, sign kept.
+// Branch-free: the normal and the subnormal encodings are both formed and one
+// is selected.
 MX_HD uint32_t mx_e4m3_code(uint32_t xb, int e) {
   const uint32_t sign = (xb >> 24) & 0x80u;
   const uint32_t ex = (xb >> 23) & 0xFFu;
   const uint32_t mx = xb & 0x7FFFFFu;
-  uint32_t m;
-  int k;                                            // |x| = m * 2^k
-  if (ex == 0u) { m = mx; k = -149; } else { m = mx | 0x800000u; k = (int)ex - 150; }
-  if (m == 0u) return sign;
-  k -= e;                                           // |y| = m * 2^k
-  const int nb = 32 - mx_clz32(m);                  // m in [2^(nb-1), 2^nb)
-  const int ey = nb - 1 + k;                        // floor(log2 |y|)
-  if (ey >= -6) {                                   // normal: 1 + 3 fraction bits
-    const uint32_t q = mx_rne_shr(m, nb - 4);       // in [8, 16]; 16 carries into the exponent
-    return sign | ((uint32_t)(ey + 7) * 8u + (q - 8u));
-  }
-  return sign | mx_rne_shr(m, -(k + 9));            // subnormal: units of 2^-9 (8 -> 0x08)
+  const uint32_t m = ex == 0u ? mx : (mx | 0x800000u);           // |x| = m * 2^k
+  const int k = (ex == 0u ? -149 : (int)ex - 150) - e;            // |y| = m * 2^k
+  const int nb = 32 - mx_clz32(m | 1u);                           // m in [2^(nb-1), 2^nb)
+  const int ey = nb - 1 + k;                                      // floor(log2 |y|)
+  // normal: 1 + 3 fraction bits; a rounding carry (q = 16) moves into the exponent
+  const uint32_t qn = mx_rne_shr(m, nb - 4);
+  const uint32_t cn = (uint32_t)(ey + 7) * 8u + (qn - 8u);
+  // subnormal: units of 2^-9 (q = 8 is the smallest normal, code 0x08)
+  const uint32_t cs = mx_rne_shr(m, -(k + 9));
+  const uint32_t code = ey >= -6 ? cn : cs;
+  return sign | (m == 0u ? 0u : code);
 }
 
 // bfloat16 bits of a float32, round to nearest even (NaN kept quiet).

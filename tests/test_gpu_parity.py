@@ -292,3 +292,38 @@ def test_argument_errors_on_device():
     h = st.host()
     w0, _ = wl.arrays()
     assert np.array_equal(h["w"], w0) and np.all(h["m"] == 0)
+
+
+def test_requant_every_float_in_key_binades():
+    """G on blocks whose amax is 448 (scale 2^0), so every other element is
+    encoded as itself: every float32 of the binades [2^-12, 2^-6) (E4M3
+    subnormals and their rounding), [1, 2) and [256, 448], both signs, against
+    torch's float32 -> float8_e4m3fn conversion (a library routine)."""
+    say("requant exhaustive binades")
+    vals = []
+    m = np.arange(1 << 23, dtype=np.uint32)
+    for ex in (-12, -11, -10, -9, -8, -7, 0, 8):
+        y = ((np.uint32(ex + 127) << 23) | m).view(np.float32)
+        if ex == 8:
+            y = y[y <= 448]
+        vals += [y, -y]
+    y = np.concatenate(vals)
+    nblk = -(-y.size // 31)
+    blocks = np.zeros((nblk, 32), np.float32)
+    blocks[:, 0] = 448.0
+    flat = blocks[:, 1:].reshape(-1)
+    flat[:y.size] = y
+    blocks[:, 1:] = flat.reshape(nblk, 31)
+    root = blocks.reshape(-1)
+    n = root.size
+    nodes = [dict(parent=-1, offset=0, rows=nblk, cols=32, row_stride=32, is_unit=False, optimizer=None,
+                  quantize=True)]
+    plan = sh.Plan(nodes, n, layout="rowmajor")
+    w = torch.from_numpy(root).cuda()
+    codes = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(plan.stats()["scale_bytes"], dtype=torch.uint8, device="cuda")
+    sh.requant_mxfp8(plan, w, codes, scales, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.all(scales == 127)
+    ref = torch.from_numpy(root).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert torch.equal(codes.cpu(), ref)
