@@ -13,8 +13,10 @@
 // operands K-contiguous, the layout the MFMA operands want:
 //   Gram    A = X X^T            P = Q = X   (r x c)
 //   poly    B = c A A + b A      P = Q = A   (A symmetric, so A A^T = A A)
-//   update  X' = a X + B X       P = B, Q = X^T (c x r), D = X; the epilogue
-//           writes X' and X'^T, the operands of the next step (no transpose pass)
+//   update  X' = a X + B X       P = B, Q = X^T (c x r); the a X term is
+//           X^T read back from the Q operand's LDS stages (no extra memory
+//           read); the epilogue writes X' and X'^T, the operands of the next
+//           step (no transpose pass)
 // A and B are symmetric: only tiles with tm <= tn are computed and each
 // off-diagonal tile is also stored mirrored.  The normalisation is folded into
 // the first step's scalars: with s = 1/(||u|| + eps), A0 = s^2 u u^T and
@@ -71,9 +73,15 @@ __device__ __forceinline__ int swz(int r) { return ((r & 31) ^ ((r & 31) >> 3)) 
 
 // acc = P[TM x K] Q[TN x K]^T, P and Q row-major with row pitch K elements
 // (bf16) starting at byte addresses gP, gQ (uniform).
-template <class C>
+//
+// CAPD (the update product, where Q = X^T and the added term is X itself):
+// D[m][n] = Q[n][dk0 + m], so the D tile passes through LDS as the Q operand of
+// the K steps covering [dk0, dk0 + TM).  While a stage is resident, the waves
+// whose rows it covers add dscale * D into their accumulators straight from
+// LDS, and the epilogue reads nothing more from memory.
+template <class C, bool CAPD = false>
 __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_t K, char *smem,
-                                          f32x16_t (&acc)[C::MBM][C::MBN]) {
+                                          f32x16_t (&acc)[C::MBM][C::MBN], int dk0 = 0, float dscale = 0.f) {
   constexpr int MBM = C::MBM, MBN = C::MBN, NW = C::NW;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
@@ -155,6 +163,31 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
     mma(fa1, fb1);
     ldfrag(sa, 3, fa1, fb1);
     mma(fa0, fb0);
+    if (CAPD) {
+      const int mb = kt * BK - dk0;                  // tile row held at K offset 0 of this stage
+      if (mb >= 0 && mb < C::TM) {
+#pragma unroll
+        for (int i = 0; i < MBM; ++i) {
+          const int bm = wm * C::WTM + i * 32;       // wave-uniform
+          if (bm >= mb && bm < mb + BK) {
+#pragma unroll
+            for (int j = 0; j < MBN; ++j) {
+              const int n = wn * C::WTN + j * 32 + lrow;
+#pragma unroll
+              for (int g4 = 0; g4 < 4; ++g4) {
+                const int kl = bm - mb + g4 * 8 + (lane >> 5) * 4;
+                const uint2 d = *reinterpret_cast<const uint2 *>(sa + C::SEGA + n * 128 +
+                                                                 (((kl >> 3) ^ swz(lrow)) << 4) + (kl & 7) * 2);
+                acc[i][j][g4 * 4 + 0] = fmaf(dscale, __uint_as_float(d.x << 16), acc[i][j][g4 * 4 + 0]);
+                acc[i][j][g4 * 4 + 1] = fmaf(dscale, __uint_as_float(d.x & 0xFFFF0000u), acc[i][j][g4 * 4 + 1]);
+                acc[i][j][g4 * 4 + 2] = fmaf(dscale, __uint_as_float(d.y << 16), acc[i][j][g4 * 4 + 2]);
+                acc[i][j][g4 * 4 + 3] = fmaf(dscale, __uint_as_float(d.y & 0xFFFF0000u), acc[i][j][g4 * 4 + 3]);
+              }
+            }
+          }
+        }
+      }
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (kt + 1 < nk) ldfrag(smem + (st ^ 1) * C::STAGE, 0, fa0, fb0);
@@ -228,9 +261,8 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[C::MBM][C::MBN]
 // laid out in the view's own orientation, so the read-modify-write of w is
 // 16 contiguous bytes per lane along the view's contiguous dimension.
 template <class C>
-__device__ __forceinline__ void final_tile(const f32x16_t (&acc)[C::MBM][C::MBN], float alpha, float beta,
-                                           const uint16_t *DT, int64_t lddt, const MuonUnit &u, float *w, float lr,
-                                           float decay, int r0, int c0, bool zero, char *smem) {
+__device__ __forceinline__ void final_tile(const f32x16_t (&acc)[C::MBM][C::MBN], float alpha, const MuonUnit &u,
+                                           float *w, float lr, float decay, int r0, int c0, bool zero, char *smem) {
   constexpr int HM = C::TM / 2;                      // rows per pass (= one wave row)
   static_assert(HM == C::WTM, "one pass per wave row");
   constexpr int PW = C::TN + 4, PT = HM + 4;         // fp32 LDS pitches (wide / tall layout)
@@ -253,11 +285,8 @@ __device__ __forceinline__ void final_tile(const f32x16_t (&acc)[C::MBM][C::MBN]
             const int li0 = i * 32 + g4 * 8 + (lane >> 5) * 4;       // row within the pass
             float x[4] = {0.f, 0.f, 0.f, 0.f};
             if (!zero) {
-              const uint2 d = *reinterpret_cast<const uint2 *>(DT + (int64_t)(c0 + lc) * lddt + r0 + h * HM + li0);
-              x[0] = fmaf(beta, __uint_as_float(d.x << 16), alpha * acc[i][j][g4 * 4 + 0]);
-              x[1] = fmaf(beta, __uint_as_float(d.x & 0xFFFF0000u), alpha * acc[i][j][g4 * 4 + 1]);
-              x[2] = fmaf(beta, __uint_as_float(d.y << 16), alpha * acc[i][j][g4 * 4 + 2]);
-              x[3] = fmaf(beta, __uint_as_float(d.y & 0xFFFF0000u), alpha * acc[i][j][g4 * 4 + 3]);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) x[q] = alpha * acc[i][j][g4 * 4 + q];
             }
             if (u.tall) {
               *reinterpret_cast<float4 *>(&lt[lc * PT + li0]) = make_float4(x[0], x[1], x[2], x[3]);
@@ -354,19 +383,18 @@ __global__ __launch_bounds__(C::NT, C::NT == 256 ? 2 : 1) void k_ns(NsArgs a) {
   } else {
     const uint16_t *XTc = (a.iter & 1) ? XT1 : XT0;
     uint16_t *XTn = (a.iter & 1) ? XT0 : XT1;
+    // X' = al (B X + a X): the a X term is taken from the Q operand in LDS
     const float al = a.iter == 0 ? s : 1.f;
-    const float be = a.iter == 0 ? a.ca * s : a.ca;
     if (STAGE == 2) {
-      gemm_core<C>(reinterpret_cast<const char *>(B + r0 * rp), reinterpret_cast<const char *>(XTc + c0 * rp),
-                      rp, smem, acc);
-      // D = X, read through X^T (the Q operand of this product)
-      store_tile<C>(acc, al, be, XTc, rp, X, cp, XTn, rp, r0, c0, smem);
+      gemm_core<C, true>(reinterpret_cast<const char *>(B + r0 * rp),
+                         reinterpret_cast<const char *>(XTc + c0 * rp), rp, smem, acc, r0, a.ca);
+      store_tile<C>(acc, al, 0.f, nullptr, 0, X, cp, XTn, rp, r0, c0, smem);
     } else {
       if (!zero)
-        gemm_core<C>(reinterpret_cast<const char *>(B + r0 * rp), reinterpret_cast<const char *>(XTc + c0 * rp),
-                        rp, smem, acc);
+        gemm_core<C, true>(reinterpret_cast<const char *>(B + r0 * rp),
+                           reinterpret_cast<const char *>(XTc + c0 * rp), rp, smem, acc, r0, a.ca);
       const MuonUnit u = a.units[unit];
-      final_tile<C>(acc, al, be, XTc, rp, u, a.w, a.lr, a.decay, r0, c0, zero, smem);
+      final_tile<C>(acc, al, u, a.w, a.lr, a.decay, r0, c0, zero, smem);
     }
   }
 }
