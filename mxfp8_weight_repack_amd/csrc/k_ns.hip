@@ -12,7 +12,8 @@
 // Every product is one "NT" contraction O = alpha P Q^T + beta D with both
 // operands K-contiguous, the layout the MFMA operands want:
 //   Gram    A = X X^T            P = Q = X   (r x c)
-//   poly    B = c A A + b A      P = Q = A   (A symmetric, so A A^T = A A)
+//   poly    B = c A A + b A      P = Q = A   (A symmetric, so A A^T = A A; the
+//                                b A term comes from the Q operand in LDS)
 //   update  X' = a X + B X       P = B, Q = X^T (c x r); the a X term is
 //           X^T read back from the Q operand's LDS stages (no extra memory
 //           read); the epilogue writes X' and X'^T, the operands of the next
@@ -46,10 +47,22 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 64;             // K elements per LDS stage
 
 __device__ __forceinline__ float bf16_to_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bfloat16 (a in the low half), one v_cvt_pk_bf16_f32:
+// round to nearest even, identical to mx_bf16_bits for every non-NaN float32
+// (checked exhaustively on the device).
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 
 // Tile configuration: TM x TN output per workgroup of WM x WN waves, each
 // wave (TM/WM) x (TN/WN) as 32x32 MFMA blocks.
@@ -62,7 +75,8 @@ struct Cfg {
   static constexpr int SEGA = TM * BK * 2, SEGB = TN * BK * 2;     // bytes of one operand stage
   static constexpr int NIA = TM / (8 * NW), NIB = TN / (8 * NW);   // DMA instructions per thread
   static constexpr int STAGE = SEGA + SEGB;
-  static constexpr int LDS = 2 * STAGE > TM * (TN + 8) * 2 ? 2 * STAGE : TM * (TN + 8) * 2;
+  static constexpr int EPI = (TM * (TN + 8) > TN * (TM + 8) ? TM * (TN + 8) : TN * (TM + 8)) * 2;
+  static constexpr int LDS = 2 * STAGE > EPI ? 2 * STAGE : EPI;
   static_assert(NW % 4 == 0 && NIA >= 1 && NIB >= 1, "tile config");
 };
 
@@ -199,49 +213,47 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
 // stored row-major to O (leading dim ldo) and, if OT, transposed to OT[col*ldt + row].
 // D is read through its transpose DT (DT[col*lddt + row] = D[row][col]): element
 // (m, n) of a 32x32 MFMA block sits in lane n + 32*((m/4)%2), register
-// (m/8)*4 + m%4, so a lane holds 4 consecutive rows of one column and both the
-// D^T read and the O^T write are 8 contiguous bytes.  The row-major O store goes
-// through LDS (bf16 tile, padded rows) so each lane writes 16 contiguous bytes.
-// smem must be free (all fragment reads done) and hold TM*(TN+8)*2 bytes.
+// (m/8)*4 + m%4, so a lane holds 4 consecutive rows of one column and the D^T
+// read is 8 contiguous bytes.  Both stores go through LDS so that every lane
+// writes 16 contiguous bytes and a wave writes whole rows: first the tile
+// row-major (2-byte LDS writes), then, for O^T, column-major (8-byte LDS writes
+// of the lane's 4 rows).  The global stores are nontemporal: they would
+// otherwise evict the operand lines that the other tiles of the launch are
+// still streaming through L2.  smem must be free (all fragment reads done) and
+// hold max(TM*(TN+8), TN*(TM+8))*2 bytes.
 template <class C>
 __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[C::MBM][C::MBN], float alpha, float beta,
                                            const uint16_t *DT, int64_t lddt, uint16_t *O, int64_t ldo, uint16_t *OT,
                                            int64_t ldt, int r0, int c0, char *smem) {
-  constexpr int LP = C::TN + 8;
+  constexpr int LP = C::TN + 8, LPT = C::TM + 8;
+  static_assert(C::TM * LP * 2 <= C::LDS && C::TN * LPT * 2 <= C::LDS, "epilogue tile fits LDS");
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave / C::WN, wn = wave % C::WN;
   uint16_t *lt = reinterpret_cast<uint16_t *>(smem);
+  uint2 hp[C::MBM][C::MBN][4];                       // packed bf16 of the lane's 4-row runs
 #pragma unroll
   for (int i = 0; i < C::MBM; ++i) {
 #pragma unroll
     for (int j = 0; j < C::MBN; ++j) {
       const int lc = wn * C::WTN + j * 32 + (lane & 31);
-      const int col = c0 + lc;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int lr0 = wm * C::WTM + i * 32 + g4 * 8 + (lane >> 5) * 4;
-        const int row0 = r0 + lr0;
         float x[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) x[q] = alpha * acc[i][j][g4 * 4 + q];
         if (DT) {
-          const uint2 d = *reinterpret_cast<const uint2 *>(DT + (int64_t)col * lddt + row0);
+          const uint2 d = *reinterpret_cast<const uint2 *>(DT + (int64_t)(c0 + lc) * lddt + r0 + lr0);
           x[0] = fmaf(beta, __uint_as_float(d.x << 16), x[0]);
           x[1] = fmaf(beta, __uint_as_float(d.x & 0xFFFF0000u), x[1]);
           x[2] = fmaf(beta, __uint_as_float(d.y << 16), x[2]);
           x[3] = fmaf(beta, __uint_as_float(d.y & 0xFFFF0000u), x[3]);
         }
-        uint32_t h[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          h[q] = mx_bf16_bits(__float_as_uint(x[q]));
-          lt[(lr0 + q) * LP + lc] = (uint16_t)h[q];
-        }
-        if (OT) {
-          uint2 pk;
-          pk.x = h[0] | (h[1] << 16);
-          pk.y = h[2] | (h[3] << 16);
-          *reinterpret_cast<uint2 *>(OT + (int64_t)col * ldt + row0) = pk;
-        }
+        const uint32_t h01 = pk_bf16(x[0], x[1]), h23 = pk_bf16(x[2], x[3]);
+        hp[i][j][g4] = make_uint2(h01, h23);
+        lt[(lr0 + 0) * LP + lc] = (uint16_t)h01;
+        lt[(lr0 + 1) * LP + lc] = (uint16_t)(h01 >> 16);
+        lt[(lr0 + 2) * LP + lc] = (uint16_t)h23;
+        lt[(lr0 + 3) * LP + lc] = (uint16_t)(h23 >> 16);
       }
     }
   }
@@ -250,8 +262,29 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[C::MBM][C::MBN]
 #pragma unroll
   for (int k = 0; k < C::TM * CH / C::NT; ++k) {
     const int id = t + C::NT * k, row = id / CH, ch = id - row * CH;
-    const uint4 v = *reinterpret_cast<const uint4 *>(&lt[row * LP + ch * 8]);
-    *reinterpret_cast<uint4 *>(O + (int64_t)(r0 + row) * ldo + c0 + ch * 8) = v;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(&lt[row * LP + ch * 8]);
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(O + (int64_t)(r0 + row) * ldo + c0 + ch * 8));
+  }
+  if (!OT) return;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < C::MBM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::MBN; ++j) {
+      const int lc = wn * C::WTN + j * 32 + (lane & 31);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int lr0 = wm * C::WTM + i * 32 + g4 * 8 + (lane >> 5) * 4;
+        *reinterpret_cast<uint2 *>(&lt[lc * LPT + lr0]) = hp[i][j][g4];
+      }
+    }
+  __syncthreads();
+  constexpr int CHT = C::TM / 8;
+#pragma unroll
+  for (int k = 0; k < C::TN * CHT / C::NT; ++k) {
+    const int id = t + C::NT * k, col = id / CHT, ch = id - col * CHT;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(&lt[col * LPT + ch * 8]);
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(OT + (int64_t)(c0 + col) * ldt + r0 + ch * 8));
   }
 }
 
@@ -376,10 +409,10 @@ __global__ __launch_bounds__(C::NT, C::NT == 256 ? 2 : 1) void k_ns(NsArgs a) {
     const float al = a.iter == 0 ? s * s : 1.f;
     store_tile<C>(acc, al, 0.f, nullptr, 0, A, rp, tl.tm != tl.tn ? A : nullptr, rp, r0, c0, smem);
   } else if (STAGE == 1) {
-    gemm_core<C>(reinterpret_cast<const char *>(A + r0 * rp), reinterpret_cast<const char *>(A + c0 * rp), rp,
-                    smem, acc);
-    // D = A, read through its transpose (A is symmetric)
-    store_tile<C>(acc, a.cc, a.cb, A, rp, B, rp, tl.tm != tl.tn ? B : nullptr, rp, r0, c0, smem);
+    // B = c (A A + (b/c) A); the A term is Q^T = A[c0.., r0..]^T, taken from LDS
+    gemm_core<C, true>(reinterpret_cast<const char *>(A + r0 * rp), reinterpret_cast<const char *>(A + c0 * rp),
+                       rp, smem, acc, r0, a.cb / a.cc);
+    store_tile<C>(acc, a.cc, 0.f, nullptr, 0, B, rp, tl.tm != tl.tn ? B : nullptr, rp, r0, c0, smem);
   } else {
     const uint16_t *XTc = (a.iter & 1) ? XT1 : XT0;
     uint16_t *XTn = (a.iter & 1) ? XT0 : XT1;
