@@ -41,7 +41,35 @@ def parse():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=25.0, help="seconds of oracle work to aim for")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="before timing, copy a 1 GiB buffer three times (a plain copy kernel of known "
+                         "size, the calibration for HBM byte counters)")
     return ap.parse_args()
+
+
+def source_digest(names):
+    """sha256 over the kernel sources a counter figure was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "mxfp8_weight_repack_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, part):
+    """HBM bytes per step of `part` ("ns_phase" or "repack") on `workload`, from
+    the counter runs recorded in profiles/traffic.json, or None when there are
+    none or the kernel sources changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(workload, {}).get(part)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("src_digest") != source_digest(rec.get("sources", [])):
+        return None
+    return rec["bytes_per_step"]
 
 
 def cpu_baseline(wl, budget_s):
@@ -122,16 +150,22 @@ def main():
     for _ in range(args.warmup):
         step += 1
         sh.update_step(plan, bufs, mhp, ahp, step, ws, ws_bytes, sp)
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        del src, dst
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record(stream)
+    for k in range(args.steps):
         step += 1
         sh.update_step(plan, bufs, mhp, ahp, step, ws, ws_bytes, sp)
-    e1.record(stream)
+        ev[k + 1].record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_step = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps))
     value = wl.params / (ms / 1e3)
 
     # per-kernel-class durations: HIP events bracketing every launch, same K steps
@@ -155,7 +189,8 @@ def main():
         roofline = {"bound": "mfma",
                     "kernel": "k_ns (Newton-Schulz contraction: every group's launches, NS phase wall time)",
                     "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                    "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                    "traffic": measured_traffic(wl.name, "ns_phase"),
                     "executed_tflop_per_step": st["ns_tile_flops"] / 1e12,
                     "dense_tflop_per_step": st["ns_flops"] / 1e12,
                     "effective_dense_tflops": st["ns_flops"] / ns_s / 1e12,
@@ -169,10 +204,13 @@ def main():
         byts = (st["quant_elems"] - fused) * 5.03125 + fused * 29.03125
         gbs = byts * args.steps / (rq_ms / 1e3) / 1e9
         repack = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": gbs / HBM_PEAK_GBS, "bytes_per_step": byts}
+                  "frac": gbs / HBM_PEAK_GBS, "bytes_per_step": byts,
+                  "traffic": measured_traffic(wl.name, "repack")}
     out = {
         "metric": METRIC, "value": value, "unit": "params/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": ms,
+        "step_ms": {"median": per_step[len(per_step) // 2], "min": per_step[0], "max": per_step[-1]},
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "params": wl.params, "root_numel": wl.root_numel,
                    "muon_units": st["n_muon_units"], "adamw_units": st["n_adamw_units"],
