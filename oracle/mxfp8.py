@@ -23,6 +23,13 @@ offset o, rows N, cols K, KB = K/32 blocks per row):
 * 'tile32x4': block (n, kb) -> o/32 + ((n//32)*(KB//4) + kb//4)*128
                                     + (n%32)*4 + kb%4,
   one 128-byte chunk per 32-row x 128-column tile, one 4-byte word per row.
+
+32 x 32 blocks ('block32x32'; [SS-HSDP §3.1 EG1] and [veScale §6] describe G
+with 32 x 32 blocks in a k-major layout): one scale per 32-row x 32-column
+block of a region (rows and cols multiples of 32, first element a multiple of
+1024), chosen by the same least-e rule over the block's 1024 elements; the
+block (bn, bk) -> o/1024 + bn*(K/32) + bk.  The same codes serve the
+transposed operand: the blocks of X^T are the transposes of X's.
 """
 
 import numpy as np
@@ -78,8 +85,38 @@ def quantize_blocks_fast(x):
     return codes.reshape(N, K), sbytes
 
 
+def quantize_blocks_32x32(x):
+    """Quantise a float32 array of shape (N, K), N and K multiples of 32, with
+    one scale per 32 x 32 block: amax over the block's 1024 elements, the
+    least-e scale, then every element's nearest E4M3FN code of x * 2**-e.
+
+    Returns (codes uint8 (N, K), scale_bytes uint8 (N/32, K/32)).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    N, K = x.shape
+    assert N % 32 == 0 and K % 32 == 0
+    codes = np.empty((N, K), dtype=np.uint8)
+    sbytes = np.empty((N // 32, K // 32), dtype=np.uint8)
+    for bn in range(N // 32):
+        for bk in range(K // 32):
+            blk = x[32 * bn:32 * bn + 32, 32 * bk:32 * bk + 32].astype(np.float64)
+            if not np.all(np.isfinite(blk)):
+                sbytes[bn, bk] = 0xFF
+                codes[32 * bn:32 * bn + 32, 32 * bk:32 * bk + 32] = 0x7F
+                continue
+            e = e8m0_exponent(np.max(np.abs(blk)))
+            sbytes[bn, bk] = e + 127
+            codes[32 * bn:32 * bn + 32, 32 * bk:32 * bk + 32] = e4m3_encode(np.ldexp(blk, -e))
+    return codes, sbytes
+
+
 def scale_index(layout, o, N, K):
-    """Index into the scale root of block (n, kb) of a region; shape (N, K/32)."""
+    """Index into the scale root of each scale of a region: shape (N, K/32)
+    for the 1 x 32 layouts, (N/32, K/32) for 'block32x32'."""
+    if layout == "block32x32":
+        bn = np.arange(N // 32, dtype=np.int64)[:, None]
+        bk = np.arange(K // 32, dtype=np.int64)[None, :]
+        return o // 1024 + bn * (K // 32) + bk
     KB = K // 32
     n = np.arange(N, dtype=np.int64)[:, None]
     kb = np.arange(KB, dtype=np.int64)[None, :]
@@ -95,10 +132,13 @@ def requant_root(w_root, resolved, layout, codes_root, scales_root, fast=True):
     """G + Tw over every quantised region of a resolved view table.
 
     Writes in place into ``codes_root`` (uint8, one per element) and
-    ``scales_root`` (uint8, one per 32 elements); bytes outside quantised
+    ``scales_root`` (uint8, one per 32 elements; one per 1024 for
+    'block32x32'); bytes outside quantised
     regions are left untouched.
     """
     q = quantize_blocks_fast if fast else quantize_blocks
+    if layout == "block32x32":
+        q = quantize_blocks_32x32
     for r in resolved:
         if not r["quantize"]:
             continue

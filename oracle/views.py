@@ -77,6 +77,8 @@ def resolve_views(nodes, root_numel, scale_layout="rowmajor"):
                 raise ViewError("SCHEMA", f"node {i}: quantised region not block aligned")
             if scale_layout == "tile32x4" and (rows % 32 or cols % 128):
                 raise ViewError("SCHEMA", f"node {i}: tile32x4 needs rows%32==0, cols%128==0")
+            if scale_layout == "block32x32" and (rows % 32 or a % 1024):
+                raise ViewError("SCHEMA", f"node {i}: block32x32 needs rows%32==0 and a 1024-aligned start")
         r = dict(nd)
         r.update(abs=a, extent=ext, row_stride=rs, rows=rows, cols=cols,
                  is_unit=is_unit, optimizer=opt if is_unit else None, quantize=q)
