@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--layout", choices=["rowmajor", "tile32x4", "block32x32"], default=None,
+                    help="scale layout (default: the workload's own); block32x32 = one scale per 32x32 block")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=25.0, help="seconds of oracle work to aim for")
     ap.add_argument("--copy-probe", action="store_true",
@@ -131,7 +133,8 @@ def main():
     torch.cuda.set_device(0)
     wl = workloads.config(args.config)
     w0, g0 = wl.arrays()
-    plan = sh.Plan(wl.nodes, wl.root_numel, layout=wl.scale_layout)
+    layout = args.layout or wl.scale_layout
+    plan = sh.Plan(wl.nodes, wl.root_numel, layout=layout)
     st = plan.stats()
     w = torch.from_numpy(w0).to(dev)
     g = torch.from_numpy(g0).to(dev)
@@ -201,7 +204,8 @@ def main():
     repack = None
     if rq_ms > 0:
         fused = st["fused_quant_elems"]
-        byts = (st["quant_elems"] - fused) * 5.03125 + fused * 29.03125
+        per_scale = 1.0 / 1024 if layout == "block32x32" else 1.0 / 32
+        byts = (st["quant_elems"] - fused) * (5.0 + per_scale) + fused * (29.0 + per_scale)
         gbs = byts * args.steps / (rq_ms / 1e3) / 1e9
         repack = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": gbs / HBM_PEAK_GBS, "bytes_per_step": byts,
@@ -215,7 +219,7 @@ def main():
         "config": {"workload": wl.name, "params": wl.params, "root_numel": wl.root_numel,
                    "muon_units": st["n_muon_units"], "adamw_units": st["n_adamw_units"],
                    "ns_groups": [[gi["r"], gi["c"], gi["n_units"]] for gi in plan.groups()],
-                   "scale_layout": wl.scale_layout, "ns_tflop_per_step": st["ns_flops"] / 1e12},
+                   "scale_layout": layout, "ns_tflop_per_step": st["ns_flops"] / 1e12},
         "roofline": roofline, "repack_roofline": repack, "components": components,
     }
     if not args.no_cpu:

@@ -79,8 +79,16 @@ enum { SSHDP_OPT_NONE = 0, SSHDP_OPT_MUON = 1, SSHDP_OPT_ADAMW = 2 };
  * scaled-MFMA tile reads in one coalesced load.  It is this library's own
  * layout (the [SS-HSDP] kernels' layout belongs to other hardware).  Both
  * layouts keep a head's scales a sub-range of its projection's when the head's
- * row count is a multiple of 32. */
-enum { SSHDP_SCALE_ROWMAJOR = 0, SSHDP_SCALE_TILE32X4 = 1 };
+ * row count is a multiple of 32.
+ *
+ * BLOCK32X32 is the other block shape [SS-HSDP §3.1 EG1] (and [veScale §6])
+ * describe: one scale per 32-row x 32-column block, the least-e rule over the
+ * block's 1024 elements, codes as above; block (bn, bk) of a region at o with
+ * K columns has its scale at  o/1024 + bn*(K/32) + bk.  The blocks of X^T are
+ * the transposes of X's, so the same codes serve the transposed operand.  The
+ * scale array then holds (root_numel + 1023)/1024 bytes, and AdamW is never
+ * fused with G (the AdamW units run first, then G). */
+enum { SSHDP_SCALE_ROWMAJOR = 0, SSHDP_SCALE_TILE32X4 = 1, SSHDP_SCALE_BLOCK32X32 = 2 };
 
 /* Plan flags. */
 enum {
@@ -100,7 +108,8 @@ enum {
  *     and cols are multiples of 4 (16-byte vectors)                (SCHEMA)
  *   a quantised region is contiguous (row_stride == cols), with cols and its
  *     first element multiples of 32; for TILE32X4 also rows % 32 == 0 and
- *     cols % 128 == 0                                               (SCHEMA)
+ *     cols % 128 == 0; for BLOCK32X32 also rows % 32 == 0 and the
+ *     first element a multiple of 1024                              (SCHEMA)
  *   units are pairwise disjoint; quantised regions too             (OVERLAP)
  * Checks run node by node in index order; overlap is checked last. */
 typedef struct {

@@ -20,7 +20,7 @@ ERROR_NAMES = {ERR_ARG: "ARG", ERR_TREE: "TREE", ERR_BOUNDS: "BOUNDS", ERR_OVERL
                ERR_SCHEMA: "SCHEMA", ERR_ALIGN: "ALIGN", ERR_WORKSPACE: "WORKSPACE", ERR_HIP: "HIP",
                ERR_STATE: "STATE"}
 OPT = {None: 0, "muon": 1, "adamw": 2}
-LAYOUT = {"rowmajor": 0, "tile32x4": 1}
+LAYOUT = {"rowmajor": 0, "tile32x4": 1, "block32x32": 2}
 PLAN_HOST_ONLY = 1
 PROF_CLASSES = ["momentum", "norm", "ns_gram", "ns_poly", "ns_update", "adamw", "adamw_requant", "requant",
                 "ns_phase"]

@@ -147,7 +147,7 @@ int sshdp_update_adamw(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_
 int sshdp_requant_mxfp8(const sshdp_plan *p, const float *w_main, uint8_t *codes, uint8_t *scales, void *stream) {
   int st = check_plan(p);
   if (st != SSHDP_OK) return st;
-  if (p->qchunks.empty()) return SSHDP_OK;
+  if (p->qchunks.empty() && p->q32tiles.empty()) return SSHDP_OK;
   st = check_quant(w_main, codes, scales);
   if (st != SSHDP_OK) return st;
   sshdp_buffers b{};
@@ -156,6 +156,7 @@ int sshdp_requant_mxfp8(const sshdp_plan *p, const float *w_main, uint8_t *codes
   b.scales = scales;
   hipStream_t s = static_cast<hipStream_t>(stream);
   Prof pr(p, 7, s);
+  if (!p->q32tiles.empty()) return hip_status(launch_quant32(*p, w_main, codes, scales, s));
   return hip_status(launch_quant(*p, 0, (int64_t)p->qchunks.size(), false, b, nullptr, 1, s));
 }
 
@@ -172,7 +173,7 @@ int sshdp_update_step(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_m
   } else if (step < 1) {
     return SSHDP_ERR_ARG;
   }
-  if (!p->qchunks.empty()) {
+  if (!p->qchunks.empty() || !p->q32tiles.empty()) {
     st = check_quant(b->w_main, b->codes, b->scales);
     if (st != SSHDP_OK) return st;
   }
@@ -194,6 +195,11 @@ int sshdp_update_step(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_m
   if (rest > 0) {
     Prof pr(p, 7, s);
     st = hip_status(launch_quant(*p, p->n_qchunks_fused, rest, false, *b, nullptr, step, s));
+  }
+  if (st != SSHDP_OK) return st;
+  if (!p->q32tiles.empty()) {
+    Prof pr(p, 7, s);
+    st = hip_status(launch_quant32(*p, b->w_main, b->codes, b->scales, s));
   }
   return st;
 }

@@ -84,6 +84,15 @@ struct QChunk {
   int32_t region;
 };
 
+// 32 x 32-block requant work item: 32 rows x up to 4 blocks of 32 columns of
+// one region, starting at element `base`; its first block's scale sits at `sidx`.
+struct Q32Tile {
+  int64_t base;
+  int64_t sidx;
+  int32_t cols;         // the region's row pitch (= columns)
+  int32_t nb;           // blocks in this tile (1..4)
+};
+
 struct DeviceTables {
   MuonUnit *munits = nullptr;
   F0Tile *f0tiles = nullptr;
@@ -91,6 +100,7 @@ struct DeviceTables {
   ASeg *aseg_unfused = nullptr;
   QRegion *qregions = nullptr;
   QChunk *qchunks = nullptr;
+  Q32Tile *q32tiles = nullptr;
   NsGroupDev *ns_groups = nullptr;
   NsTile *ns_tiles[kMaxLanes][3][2] = {};   // [lane][stage: Gram, poly, update][tile: 128, 256]
 };
@@ -117,6 +127,7 @@ struct sshdp_plan {
   std::vector<sshdp::QRegion> qregions;
   std::vector<sshdp::QChunk> qchunks;   // fused-eligible chunks first
   int64_t n_qchunks_fused = 0;
+  std::vector<sshdp::Q32Tile> q32tiles; // BLOCK32X32 layout: all requant work
   size_t ws_uscale = 0, ws_partials = 0, ws_bytes = 0;
   sshdp_plan_stats stats{};
   bool host_only = true;
@@ -145,4 +156,5 @@ hipError_t launch_adamw(const ASeg *segs, int64_t nseg, const sshdp_buffers &b, 
                         int64_t step, hipStream_t s);
 hipError_t launch_quant(const sshdp_plan &p, int64_t first, int64_t count, bool fused, const sshdp_buffers &b,
                         const sshdp_adamw_hp *hp, int64_t step, hipStream_t s);
+hipError_t launch_quant32(const sshdp_plan &p, const float *w, uint8_t *codes, uint8_t *scales, hipStream_t s);
 }  // namespace sshdp

@@ -306,6 +306,55 @@ __global__ __launch_bounds__(256) void k_quant(const QChunk *__restrict__ chunks
   }
 }
 
+// G with one scale per 32 x 32 block.  A workgroup takes one tile: 32 rows of
+// up to 4 blocks (128 columns).  Lane t owns 4 consecutive columns (4*(t%32))
+// of rows t/32 + 8p, p = 0..3, so a row of the tile is 32 lanes x 16 bytes.
+// The block amax: a lane's 16 values, then lanes of the same block and row
+// group (xor 1, 2, 4), then the two row groups of a wave (xor 32), then the 4
+// waves through LDS.  Codes as in k_quant (hardware E4M3FN convert of the
+// exactly scaled value); the scale byte is written once per block.
+__global__ __launch_bounds__(256) void k_quant32(const Q32Tile *__restrict__ tiles, const float *__restrict__ w,
+                                                 uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+  __shared__ uint32_t red[4][4];
+  const Q32Tile q = tiles[blockIdx.x];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int c4 = t & 31, blk = c4 >> 3, rg = t >> 5;
+  const bool act = blk < q.nb;
+  float4 wv[4];
+  uint32_t a = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    wv[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (act) wv[p] = *reinterpret_cast<const float4 *>(w + q.base + (int64_t)(rg + 8 * p) * q.cols + 4 * c4);
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+    a = max(a, max(max(fbits(wv[p].x) & 0x7FFFFFFFu, fbits(wv[p].y) & 0x7FFFFFFFu),
+                   max(fbits(wv[p].z) & 0x7FFFFFFFu, fbits(wv[p].w) & 0x7FFFFFFFu)));
+  a = max(a, (uint32_t)__shfl_xor((int)a, 1));
+  a = max(a, (uint32_t)__shfl_xor((int)a, 2));
+  a = max(a, (uint32_t)__shfl_xor((int)a, 4));
+  a = max(a, (uint32_t)__shfl_xor((int)a, 32));
+  if (lane < 32 && (lane & 7) == 0) red[wave][blk] = a;
+  __syncthreads();
+  a = max(max(red[0][blk], red[1][blk]), max(red[2][blk], red[3][blk]));
+  if (!act) return;
+  const uint32_t sb = mx_scale_byte(a);
+  const int ex = 127 - (int)sb;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t packed = 0x7F7F7F7Fu;
+    if (sb != 0xFFu) {
+      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(wv[p].x, ex), ldexpf(wv[p].y, ex), 0, false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(wv[p].z, ex), ldexpf(wv[p].w, ex), pk, true);
+      packed = (uint32_t)pk;
+    }
+    __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t *>(codes + q.base + (int64_t)(rg + 8 * p) * q.cols +
+                                                                     4 * c4));
+  }
+  if (rg == 0 && (c4 & 7) == 0) scales[q.sidx + blk] = (uint8_t)sb;
+}
+
 AdamConst adam_const(const sshdp_adamw_hp &hp, int64_t step) {
   AdamConst c;
   c.b1 = hp.beta1;
@@ -360,6 +409,15 @@ hipError_t launch_quant(const sshdp_plan &p, int64_t first, int64_t count, bool 
   else
     hipLaunchKernelGGL(k_quant<false>, dim3((unsigned)count), dim3(256), 0, s, p.d.qchunks + first, p.d.qregions,
                        tile, b.w_main, nullptr, nullptr, nullptr, b.codes, b.scales, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant32(const sshdp_plan &p, const float *w, uint8_t *codes, uint8_t *scales, hipStream_t s) {
+  const int64_t n = (int64_t)p.q32tiles.size();
+  for (int64_t first = 0; first < n; first += 0x7FFFFFFF) {
+    const int64_t cnt = std::min<int64_t>(n - first, 0x7FFFFFFF);
+    hipLaunchKernelGGL(k_quant32, dim3((unsigned)cnt), dim3(256), 0, s, p.d.q32tiles + first, w, codes, scales);
+  }
   return hipGetLastError();
 }
 

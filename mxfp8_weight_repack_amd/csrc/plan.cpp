@@ -71,6 +71,7 @@ int validate(const sshdp_node *nodes, int32_t n, int64_t root_numel, int layout,
     if (nd.quantize) {
       if (rs != nd.cols || nd.cols % 32 || a % 32) return SSHDP_ERR_SCHEMA;
       if (layout == SSHDP_SCALE_TILE32X4 && (nd.rows % 32 || nd.cols % 128)) return SSHDP_ERR_SCHEMA;
+      if (layout == SSHDP_SCALE_BLOCK32X32 && (nd.rows % 32 || a % 1024)) return SSHDP_ERR_SCHEMA;
       if (nd.cols > (1 << 30)) return SSHDP_ERR_SCHEMA;
     }
     abs[i] = a;
@@ -306,6 +307,15 @@ void build_elementwise(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
     const int64_t a = p.node_abs[i], len = nd.rows * nd.cols;
     p.qregions.push_back({a, nd.rows, (int32_t)nd.cols, 0});
     p.stats.quant_elems += len;
+    if (p.opts.scale_layout == SSHDP_SCALE_BLOCK32X32) {
+      // 32-row strips cut into tiles of up to 4 blocks; AdamW is not fused here
+      const int64_t kb = nd.cols / 32;
+      for (int64_t br = 0; br < nd.rows / 32; ++br)
+        for (int64_t b0 = 0; b0 < kb; b0 += 4)
+          p.q32tiles.push_back({a + br * 32 * nd.cols + b0 * 32, a / 1024 + br * kb + b0, (int32_t)nd.cols,
+                                (int32_t)std::min<int64_t>(4, kb - b0)});
+      continue;
+    }
     // unit intervals intersecting the region
     auto it = std::lower_bound(units.begin(), units.end(), a,
                                [](const Interval &u, int64_t x) { return u.start + u.len <= x; });
@@ -380,7 +390,7 @@ size_t table_bytes(const std::vector<T> &v) { return round_up((int64_t)(v.size()
 int upload(sshdp_plan &p) {
   const size_t total = table_bytes(p.munits) + table_bytes(p.f0tiles) + table_bytes(p.aseg_all) +
                        table_bytes(p.aseg_unfused) + table_bytes(p.qregions) + table_bytes(p.qchunks) +
-                       table_bytes(p.ns_groups) + 256;
+                       table_bytes(p.q32tiles) + table_bytes(p.ns_groups) + 256;
   size_t tiles_total = 0;
   for (auto &ln : p.ns_tiles)
     for (auto &st : ln)
@@ -402,6 +412,7 @@ int upload(sshdp_plan &p) {
   put(p.aseg_unfused, p.d.aseg_unfused);
   put(p.qregions, p.d.qregions);
   put(p.qchunks, p.d.qchunks);
+  put(p.q32tiles, p.d.q32tiles);
   put(p.ns_groups, p.d.ns_groups);
   for (int ln = 0; ln < kMaxLanes; ++ln)
     for (int st = 0; st < 3; ++st)
@@ -462,7 +473,8 @@ int sshdp_plan_views(const sshdp_node *nodes, int32_t n_nodes, int64_t root_nume
   sshdp_plan_opts o;
   if (opts) o = *opts; else sshdp_default_opts(&o);
   if (o.ns_steps < 1 || o.ns_steps > 64 || (o.scale_layout != SSHDP_SCALE_ROWMAJOR &&
-      o.scale_layout != SSHDP_SCALE_TILE32X4) || o.muon_scale_mode < 0 || o.muon_scale_mode > 2 ||
+      o.scale_layout != SSHDP_SCALE_TILE32X4 && o.scale_layout != SSHDP_SCALE_BLOCK32X32) ||
+      o.muon_scale_mode < 0 || o.muon_scale_mode > 2 ||
       !(o.ns_eps >= 0.0f) || (o.flags & ~1u))
     return SSHDP_ERR_ARG;
   std::vector<int64_t> abs, ext;
@@ -474,7 +486,7 @@ int sshdp_plan_views(const sshdp_node *nodes, int32_t n_nodes, int64_t root_nume
   p->opts = o;
   p->node_abs = abs;
   p->stats.root_numel = root_numel;
-  p->stats.scale_bytes = (root_numel + 31) / 32;
+  p->stats.scale_bytes = o.scale_layout == SSHDP_SCALE_BLOCK32X32 ? (root_numel + 1023) / 1024 : (root_numel + 31) / 32;
   p->stats.n_nodes = n_nodes;
   for (int32_t i = 0; i < n_nodes; ++i) p->stats.n_units += nodes[i].is_unit ? 1 : 0;
   build_muon(*p, nodes, n_nodes);

@@ -61,7 +61,8 @@ def oracle_step(wl, layout, w, g, m, v, step=1, hp=None, **kw):
     the per-unit float64 Newton-Schulz directions."""
     w = w.copy(); m = m.copy(); v = v.copy()
     codes = np.zeros(wl.root_numel, np.uint8)
-    scales = np.zeros((wl.root_numel + 31) // 32, np.uint8)
+    scales = np.zeros((wl.root_numel + 1023) // 1024 if layout == "block32x32" else (wl.root_numel + 31) // 32,
+                      np.uint8)
     dirs = oracle.update_step(wl.nodes, wl.root_numel, w, g, m, v, codes, scales, step, hp=hp,
                               layout=layout, keep_v=True, **kw)
     return dict(w=w, m=m, v=v, codes=codes, scales=scales), dirs

@@ -41,16 +41,18 @@ def _plan(nodes, n, layout="rowmajor"):
     return sh.Plan(nodes, n, layout=layout, host_only=True)
 
 
-def _random_tree(rng, N):
+def _random_tree(rng, N, blocks32=False):
     nodes = []
     for i in range(int(rng.integers(1, 7))):
         p = int(rng.integers(-1, i)) if i else -1
         if rng.uniform() < 0.05:
             p = int(rng.integers(-3, i + 2))
         rows = int(rng.integers(0 if rng.uniform() < 0.03 else 1, 6))
+        if blocks32 and rng.uniform() < 0.5:
+            rows = int(rng.choice([32, 64, 48]))
         cols = int(rng.choice([4, 8, 12, 32, 64, 96, 128, 5, 37]))
         rs = cols + int(rng.choice([0, 0, 0, 4, 32, -2]))
-        off = int(rng.choice([0, 4, 8, 32, 64, 3, 128, 256]))
+        off = int(rng.choice([0, 4, 8, 32, 64, 3, 128, 256] + ([1024, 2048, 3072] if blocks32 else [])))
         unit = rng.uniform() < 0.6
         opt = rng.choice(["muon", "adamw"]) if unit else None
         if unit and rng.uniform() < 0.03:
@@ -61,19 +63,20 @@ def _random_tree(rng, N):
     return nodes
 
 
-@pytest.mark.parametrize("layout", ["rowmajor", "tile32x4"])
+@pytest.mark.parametrize("layout", ["rowmajor", "tile32x4", "block32x32"])
 def test_planner_agrees_with_oracle_rules_on_random_trees(layout):
-    rng = np.random.default_rng(42 if layout == "rowmajor" else 43)
+    rng = np.random.default_rng({"rowmajor": 42, "tile32x4": 43, "block32x32": 44}[layout])
     n_ok = n_err = 0
+    root = 16384 if layout == "block32x32" else 2048
     for _ in range(3000):
-        nodes = _random_tree(rng, 2048)
+        nodes = _random_tree(rng, root, blocks32=layout == "block32x32")
         try:
-            res = oracle.resolve_views(nodes, 2048, layout)
+            res = oracle.resolve_views(nodes, root, layout)
             exp = None
         except ViewError as e:
             exp = e.code
         try:
-            p = _plan(nodes, 2048, layout)
+            p = _plan(nodes, root, layout)
             got = None
         except sh.SshdpError as e:
             got = e.name
@@ -119,6 +122,15 @@ def test_planner_groups_and_stats_on_workloads():
     wl = workloads.config(2, small=True)
     st = _plan(wl.nodes, wl.root_numel, "tile32x4").stats()
     assert st["fused_quant_elems"] == 0
+    # one scale per 32x32 block: 1/1024 of the root, never fused with AdamW
+    for cid in (1, 2, 3, 5):
+        wl = workloads.config(cid)
+        st = _plan(wl.nodes, wl.root_numel, "block32x32").stats()
+        assert st["scale_bytes"] == (wl.root_numel + 1023) // 1024 and st["fused_quant_elems"] == 0
+    wl = workloads.config(4, small=True)
+    with pytest.raises(sh.SshdpError) as e:
+        _plan(wl.nodes, wl.root_numel, "block32x32")
+    assert e.value.name == "SCHEMA"
 
 
 def test_planner_argument_errors():

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle.views import resolve_views, unit_indices
+from oracle.views import ViewError, resolve_views, unit_indices
 import mxfp8_weight_repack_amd as sh
 import workloads
 from gpu_util import DeviceState, oracle_step, rel_fro, say, MUON, ADAM
@@ -82,11 +82,16 @@ def _specials(w, wl):
 
 
 @pytest.mark.parametrize("case", ["c1", "c2s", "c3s", "c4s", "c5s", "ragged"])
-@pytest.mark.parametrize("layout", ["rowmajor", "tile32x4"])
+@pytest.mark.parametrize("layout", ["rowmajor", "tile32x4", "block32x32"])
 def test_requant_bit_exact(case, layout):
     wl = workloads.ragged_mix() if case == "ragged" else workloads.config(int(case[1]), small=case.endswith("s"))
     if layout == "tile32x4" and wl.scale_layout != "tile32x4":
         pytest.skip("workload has quantised regions that are not 32x128 tiles")
+    if layout == "block32x32":
+        try:
+            resolve_views(wl.nodes, wl.root_numel, layout)
+        except ViewError:
+            pytest.skip("workload has quantised regions that are not whole 32x32 blocks")
     say(f"requant {wl.name} {layout}")
     w0, _ = wl.arrays()
     w = _specials(w0, wl)
@@ -166,15 +171,15 @@ def check_step(wl, layout, h, ref, dirs, w0, muon_lr=MUON["lr"], units=None):
         assert np.all(h["m"][~touched] == 0) and np.all(h["v"][~touched] == 0)
     # G on the GPU-updated weight: bit-exact against the oracle's quantiser
     codes = np.zeros(wl.root_numel, np.uint8)
-    scales = np.zeros((wl.root_numel + 31) // 32, np.uint8)
+    scales = np.zeros(h["scales"].size, np.uint8)
     oracle.requant_root(h["w"], res, layout, codes, scales)
     qmask = np.zeros(wl.root_numel, bool)
+    smask = np.zeros(scales.size, bool)
     for r in res:
         if r["quantize"]:
             qmask[unit_indices(r).ravel()] = True
+            smask[oracle.scale_index(layout, r["abs"], r["rows"], r["cols"]).ravel()] = True
     assert np.array_equal(h["codes"][qmask], codes[qmask])
-    smask = np.zeros(scales.size, bool)
-    smask[np.nonzero(qmask)[0] // 32] = True
     assert np.array_equal(h["scales"][smask], scales[smask])
     return worst
 
@@ -191,6 +196,22 @@ def test_update_step_parity(case):
     ref, dirs = oracle_step(wl, wl.scale_layout, w0, g, z, z, 1)
     worst = check_step(wl, wl.scale_layout, h, ref, dirs, w0)
     say(f"  worst NS rel-Frobenius {worst:.3e}")
+
+
+@pytest.mark.parametrize("case", ["c1", "c2s", "c3s"])
+def test_update_step_parity_block32x32(case):
+    """The whole step with one scale per 32x32 block: AdamW runs unfused, then
+    G on the updated weights; codes and scales bit-exact."""
+    wl = _wl(case)
+    say(f"update_step {wl.name} (block32x32)")
+    w0, g = wl.arrays()
+    st = DeviceState(wl, layout="block32x32")
+    assert st.stats["scale_bytes"] == (wl.root_numel + 1023) // 1024
+    st.step(1)
+    h = st.host()
+    z = np.zeros_like(w0)
+    ref, dirs = oracle_step(wl, "block32x32", w0, g, z, z, 1)
+    check_step(wl, "block32x32", h, ref, dirs, w0)
 
 
 def test_update_step_equals_separate_calls_bitwise():
