@@ -82,6 +82,7 @@ struct QChunk {
   int64_t lo, hi;
   int32_t n;
   int32_t region;
+  int32_t row0, col0;   // region row and column of `base` (for the TILE32X4 scale index)
 };
 
 // 32 x 32-block requant work item: 32 rows x up to 4 blocks of 32 columns of

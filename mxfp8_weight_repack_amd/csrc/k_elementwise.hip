@@ -214,10 +214,13 @@ __device__ __forceinline__ void quant_store(const float4 &wv, int64_t e, bool li
   if ((t & 7) == 0) {
     int64_t idx = e >> 5;
     if (tile_layout) {
+      // element e sits (e - base) < kChunk past the chunk's first element, whose
+      // region row/column the planner stored: a 32-bit division by the row length
       const QRegion r = regions[q.region];
-      const int64_t rel = e - r.abs;
-      const int64_t n = rel / r.cols;
-      const int64_t kb = (rel - n * r.cols) >> 5;
+      const uint32_t col = (uint32_t)q.col0 + (uint32_t)(e - q.base);
+      const uint32_t dn = col / (uint32_t)r.cols;
+      const int64_t n = (int64_t)q.row0 + dn;
+      const uint32_t kb = (col - dn * (uint32_t)r.cols) >> 5;
       const int64_t KB = r.cols >> 5;
       idx = (r.abs >> 5) + ((n >> 5) * (KB >> 2) + (kb >> 2)) * 128 + (n & 31) * 4 + (kb & 3);
     }

@@ -72,7 +72,7 @@ int validate(const sshdp_node *nodes, int32_t n, int64_t root_numel, int layout,
       if (rs != nd.cols || nd.cols % 32 || a % 32) return SSHDP_ERR_SCHEMA;
       if (layout == SSHDP_SCALE_TILE32X4 && (nd.rows % 32 || nd.cols % 128)) return SSHDP_ERR_SCHEMA;
       if (layout == SSHDP_SCALE_BLOCK32X32 && (nd.rows % 32 || a % 1024)) return SSHDP_ERR_SCHEMA;
-      if (nd.cols > (1 << 30)) return SSHDP_ERR_SCHEMA;
+      if (nd.cols > (1 << 30) || nd.rows > INT32_MAX) return SSHDP_ERR_SCHEMA;
     }
     abs[i] = a;
     ext[i] = e;
@@ -355,6 +355,8 @@ void build_elementwise(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
       q.base = pos;
       q.n = (int32_t)(end - pos);
       q.region = ri;
+      q.row0 = (int32_t)((pos - a) / nd.cols);
+      q.col0 = (int32_t)((pos - a) % nd.cols);
       q.lo = q.hi = pos;
       if (eligible) {
         for (const Interval &iv : inside) {
