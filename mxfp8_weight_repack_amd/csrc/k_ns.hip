@@ -50,6 +50,8 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 64;             // K elements per LDS stage
+// Buffer resource word 3 for raw (untyped) gfx9-family buffer loads.
+constexpr int kBufWord3 = 0x00020000;
 
 __device__ __forceinline__ float bf16_to_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
@@ -97,15 +99,22 @@ template <class C, bool CAPD = false>
 __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_t K, char *smem,
                                           f32x16_t (&acc)[C::MBM][C::MBN], int dk0 = 0, float dscale = 0.f) {
   constexpr int MBM = C::MBM, MBN = C::MBN, NW = C::NW;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: LDS targets and offsets in SGPRs
   const int wm = wave / C::WN, wn = wave % C::WN;
 
-  // DMA: instruction i of wave w fills rows 8*(NW*i + w) .. +7, 8 lanes per row;
-  // lane i of an instruction lands at LDS base + 16*i
+  // DMA: buffer loads straight into LDS.  Instruction i of wave w fills rows
+  // 8*(NW*i + w) .. +7 of a stage segment, 8 lanes per 128-byte row; lane i of
+  // an instruction lands at LDS base + 16*i (M0).  The per-lane offset is fixed,
+  // the K position and row block go in the scalar offset.  Each operand's
+  // buffer resource covers exactly its TM (TN) x K panel.
   const int drow = 8 * wave + (lane >> 3);
   const int dchunk = (lane & 7) ^ swz(drow);         // rows drow + 8*NW*i share the swizzle
-  const uint32_t loff = (uint32_t)(drow * K + dchunk * 8) * 2u;
-  const int dlds = wave * 1024;
+  const int voff = (drow * (int)K + dchunk * 8) * 2;
+  const __amdgpu_buffer_rsrc_t rP =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(gP), 0, (int)(C::TM * K * 2), kBufWord3);
+  const __amdgpu_buffer_rsrc_t rQ =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(gQ), 0, (int)(C::TN * K * 2), kBufWord3);
 
   // fragment reads: lane holds row (lane & 31) of a 32-row block, logical chunk 2 kk + (lane >> 5)
   const int lrow = lane & 31;
@@ -121,22 +130,19 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  auto dma = [&](int stage, int64_t k0) __attribute__((always_inline)) {
-    char *sa = smem + stage * C::STAGE;
+  auto dma_p = [&](int stage, int k0) __attribute__((always_inline)) {
+    char *sa = smem + stage * C::STAGE + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < C::NIA; ++i) {
-      const int64_t ob = ((int64_t)i * 8 * NW * K + k0) * 2;
-      __builtin_amdgcn_global_load_lds(gP + ob + loff,
-                                       (__attribute__((address_space(3))) void *)(sa + dlds + i * NW * 1024), 16, 0,
-                                       0);
-    }
+    for (int i = 0; i < C::NIA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (__attribute__((address_space(3))) void *)(sa + i * NW * 1024),
+                                               16, voff, (i * 8 * NW * (int)K + k0) * 2, 0, 0);
+  };
+  auto dma_q = [&](int stage, int k0) __attribute__((always_inline)) {
+    char *sa = smem + stage * C::STAGE + C::SEGA + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < C::NIB; ++i) {
-      const int64_t ob = ((int64_t)i * 8 * NW * K + k0) * 2;
-      __builtin_amdgcn_global_load_lds(gQ + ob + loff,
-                                       (__attribute__((address_space(3))) void *)(sa + C::SEGA + dlds + i * NW * 1024),
-                                       16, 0, 0);
-    }
+    for (int i = 0; i < C::NIB; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (__attribute__((address_space(3))) void *)(sa + i * NW * 1024),
+                                               16, voff, (i * 8 * NW * (int)K + k0) * 2, 0, 0);
   };
   bf16x8_t fa0[MBM], fb0[MBN], fa1[MBM], fb1[MBN];
   auto ldfrag = [&](const char *sa, int kk, bf16x8_t(&fa_)[MBM], bf16x8_t(&fb_)[MBN]) __attribute__((always_inline)) {
@@ -146,37 +152,46 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
     for (int j = 0; j < MBN; ++j)
       fb_[j] = *reinterpret_cast<const bf16x8_t *>(sa + C::SEGA + rb + j * 32 * 128 + cofs[kk]);
   };
-  auto mma = [&](bf16x8_t(&fa_)[MBM], bf16x8_t(&fb_)[MBN]) __attribute__((always_inline)) {
+  // one slice's MFMAs, each followed by one fragment read of the next slice;
+  // NV of the stage's buffer loads are spread over the first MFMAs
+  auto mma = [&](bf16x8_t(&fa_)[MBM], bf16x8_t(&fb_)[MBN], int nv) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < MBM; ++i)
 #pragma unroll
       for (int j = 0; j < MBN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_[i], fb_[j], acc[i][j], 0, 0, 0);
-    // each MFMA followed by one fragment read of the next slice
     constexpr int NR = MBM + MBN, NM = MBM * MBN;
 #pragma unroll
-    for (int i = 0; i < (NR < NM ? NR : NM); ++i) {
+    for (int i = 0; i < NM; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < nv) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-    if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
   };
-
   const int nk = (int)(K / BK);
-  dma(0, 0);
+  dma_p(0, 0);
+  dma_q(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   ldfrag(smem, 0, fa0, fb0);
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
-    if (kt + 1 < nk) dma(st ^ 1, (int64_t)(kt + 1) * BK);
+    // the last step reloads its own K slice into the idle stage (never read),
+    // so no branch splits the body: each slice's MFMAs interleave with the next
+    // slice's fragment reads and with half the next stage's buffer loads
+    const int kn = (kt + 1 < nk ? kt + 1 : kt) * BK;
     const char *sa = smem + st * C::STAGE;
+    dma_p(st ^ 1, kn);
     ldfrag(sa, 1, fa1, fb1);
-    mma(fa0, fb0);
+    mma(fa0, fb0, C::NIA);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_q(st ^ 1, kn);
     ldfrag(sa, 2, fa0, fb0);
-    mma(fa1, fb1);
+    mma(fa1, fb1, C::NIB);
+    __builtin_amdgcn_sched_barrier(0);
     ldfrag(sa, 3, fa1, fb1);
-    mma(fa0, fb0);
+    mma(fa0, fb0, 0);
+    __builtin_amdgcn_sched_barrier(0);
     if (CAPD) {
       const int mb = kt * BK - dk0;                  // tile row held at K offset 0 of this stage
       if (mb >= 0 && mb < C::TM) {
@@ -204,8 +219,8 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kt + 1 < nk) ldfrag(smem + (st ^ 1) * C::STAGE, 0, fa0, fb0);
-    mma(fa1, fb1);
+    ldfrag(smem + (st ^ 1) * C::STAGE, 0, fa0, fb0);   // after the last step: unused
+    mma(fa1, fb1, 0);
   }
 }
 
