@@ -40,6 +40,7 @@
 
 #include "internal.h"
 #include "mx_codec.h"
+#include "lds_swizzle.h"
 #include "tile_map.h"
 
 namespace sshdp {
@@ -49,7 +50,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int BK = 64;             // K elements per LDS stage
 // Buffer resource word 3 for raw (untyped) gfx9-family buffer loads.
 constexpr int kBufWord3 = 0x00020000;
 
@@ -67,25 +67,31 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
 }
 
 // Tile configuration: TM x TN output per workgroup of WM x WN waves, each
-// wave (TM/WM) x (TN/WN) as 32x32 MFMA blocks.
-template <int TM_, int TN_, int WM_, int WN_>
+// wave (TM/WM) x (TN/WN) as 32x32 MFMA blocks; K moves through a ring of NST
+// LDS stages of BK elements.  Both shipped configurations use BK = 64 and two
+// stages: on the raw contraction, BK = 32 with a 4- or 6-stage ring and a
+// 3-stage ring at BK = 64 (one workgroup per CU) all measured 15-30% slower.
+template <int TM_, int TN_, int WM_, int WN_, int BK_ = 64, int NST_ = 2>
 struct Cfg {
-  static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+  static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_, BK = BK_, NST = NST_;
   static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int WTM = TM / WM, WTN = TN / WN;
   static constexpr int MBM = WTM / 32, MBN = WTN / 32;
-  static constexpr int SEGA = TM * BK * 2, SEGB = TN * BK * 2;     // bytes of one operand stage
-  static constexpr int NIA = TM / (8 * NW), NIB = TN / (8 * NW);   // DMA instructions per thread
+  static constexpr int RB = BK * 2;                                // bytes per LDS row
+  static constexpr int CPR = RB / 16, RPI = 1024 / RB;             // 16-byte chunks per row, rows per load
+  static constexpr int KS = BK / 16;                               // MFMA K slices per stage
+  static constexpr int SEGA = TM * RB, SEGB = TN * RB;             // bytes of one operand stage
+  static constexpr int NIA = TM / (RPI * NW), NIB = TN / (RPI * NW);   // buffer loads per wave per stage
+  static constexpr int NV = NIA + NIB;
   static constexpr int STAGE = SEGA + SEGB;
   static constexpr int EPI = (TM * (TN + 8) > TN * (TM + 8) ? TM * (TN + 8) : TN * (TM + 8)) * 2;
-  static constexpr int LDS = 2 * STAGE > EPI ? 2 * STAGE : EPI;
-  static_assert(NW % 4 == 0 && NIA >= 1 && NIB >= 1, "tile config");
+  static constexpr int LDS = NST * STAGE > EPI ? NST * STAGE : EPI;
+  static_assert(NW % 4 == 0 && NIA >= 1 && NIB >= 1 && (BK == 64 || BK == 32) && NST >= 2, "tile config");
+  static_assert((NST - 2) * NV <= 63, "vmcnt range");
 };
 
-// Physical 16-byte chunk = logical chunk ^ swz(row): any 8 consecutive rows
-// (and any 16) of a 32-row block read at one logical chunk land on distinct
-// 16-byte bank groups.
-__device__ __forceinline__ int swz(int r) { return ((r & 31) ^ ((r & 31) >> 3)) & 7; }
+template <int BK>
+__device__ __forceinline__ int swz(int r) { return lds_swz<BK>(r); }
 
 // acc = P[TM x K] Q[TN x K]^T, P and Q row-major with row pitch K elements
 // (bf16) starting at byte addresses gP, gQ (uniform).
@@ -98,18 +104,19 @@ __device__ __forceinline__ int swz(int r) { return ((r & 31) ^ ((r & 31) >> 3)) 
 template <class C, bool CAPD = false>
 __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_t K, char *smem,
                                           f32x16_t (&acc)[C::MBM][C::MBN], int dk0 = 0, float dscale = 0.f) {
-  constexpr int MBM = C::MBM, MBN = C::MBN, NW = C::NW;
+  constexpr int MBM = C::MBM, MBN = C::MBN, NW = C::NW, BK = C::BK, RB = C::RB, CPR = C::CPR, RPI = C::RPI;
+  constexpr int NST = C::NST;
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: LDS targets and offsets in SGPRs
   const int wm = wave / C::WN, wn = wave % C::WN;
 
-  // DMA: buffer loads straight into LDS.  Instruction i of wave w fills rows
-  // 8*(NW*i + w) .. +7 of a stage segment, 8 lanes per 128-byte row; lane i of
-  // an instruction lands at LDS base + 16*i (M0).  The per-lane offset is fixed,
-  // the K position and row block go in the scalar offset.  Each operand's
-  // buffer resource covers exactly its TM (TN) x K panel.
-  const int drow = 8 * wave + (lane >> 3);
-  const int dchunk = (lane & 7) ^ swz(drow);         // rows drow + 8*NW*i share the swizzle
+  // DMA: buffer loads straight into LDS.  Load i of wave w fills rows
+  // RPI*(NW*i + w) .. +RPI-1 of a stage segment, CPR lanes per row; lane i of a
+  // load lands at LDS base + 16*i (M0).  The per-lane offset is fixed, the K
+  // position and row block go in the scalar offset.  Each operand's buffer
+  // resource covers exactly its TM (TN) x K panel.
+  const int drow = RPI * wave + lane / CPR;
+  const int dchunk = (lane % CPR) ^ swz<BK>(drow);   // rows drow + RPI*NW*i share the swizzle
   const int voff = (drow * (int)K + dchunk * 8) * 2;
   const __amdgpu_buffer_rsrc_t rP =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(gP), 0, (int)(C::TM * K * 2), kBufWord3);
@@ -118,10 +125,10 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
 
   // fragment reads: lane holds row (lane & 31) of a 32-row block, logical chunk 2 kk + (lane >> 5)
   const int lrow = lane & 31;
-  const int ra = (wm * C::WTM + lrow) * 128, rb = (wn * C::WTN + lrow) * 128;
-  int cofs[4];
+  const int ra = (wm * C::WTM + lrow) * RB, rb = (wn * C::WTN + lrow) * RB;
+  int cofs[C::KS];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) cofs[kk] = ((2 * kk + (lane >> 5)) ^ swz(lrow)) * 16;
+  for (int kk = 0; kk < C::KS; ++kk) cofs[kk] = ((2 * kk + (lane >> 5)) ^ swz<BK>(lrow)) * 16;
 
 #pragma unroll
   for (int i = 0; i < MBM; ++i)
@@ -135,63 +142,83 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
 #pragma unroll
     for (int i = 0; i < C::NIA; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (__attribute__((address_space(3))) void *)(sa + i * NW * 1024),
-                                               16, voff, (i * 8 * NW * (int)K + k0) * 2, 0, 0);
+                                               16, voff, (i * RPI * NW * (int)K + k0) * 2, 0, 0);
   };
   auto dma_q = [&](int stage, int k0) __attribute__((always_inline)) {
     char *sa = smem + stage * C::STAGE + C::SEGA + wave * 1024;
 #pragma unroll
     for (int i = 0; i < C::NIB; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (__attribute__((address_space(3))) void *)(sa + i * NW * 1024),
-                                               16, voff, (i * 8 * NW * (int)K + k0) * 2, 0, 0);
+                                               16, voff, (i * RPI * NW * (int)K + k0) * 2, 0, 0);
   };
   bf16x8_t fa0[MBM], fb0[MBN], fa1[MBM], fb1[MBN];
   auto ldfrag = [&](const char *sa, int kk, bf16x8_t(&fa_)[MBM], bf16x8_t(&fb_)[MBN]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < MBM; ++i) fa_[i] = *reinterpret_cast<const bf16x8_t *>(sa + ra + i * 32 * 128 + cofs[kk]);
+    for (int i = 0; i < MBM; ++i) fa_[i] = *reinterpret_cast<const bf16x8_t *>(sa + ra + i * 32 * RB + cofs[kk]);
 #pragma unroll
     for (int j = 0; j < MBN; ++j)
-      fb_[j] = *reinterpret_cast<const bf16x8_t *>(sa + C::SEGA + rb + j * 32 * 128 + cofs[kk]);
+      fb_[j] = *reinterpret_cast<const bf16x8_t *>(sa + C::SEGA + rb + j * 32 * RB + cofs[kk]);
   };
-  // one slice's MFMAs, each followed by one fragment read of the next slice;
-  // NV of the stage's buffer loads are spread over the first MFMAs
-  auto mma = [&](bf16x8_t(&fa_)[MBM], bf16x8_t(&fb_)[MBN], int nv) __attribute__((always_inline)) {
+  // one slice's MFMAs, each followed by one fragment read of the next slice
+  // (nr of them) and one buffer load (nv of them)
+  auto mma = [&](bf16x8_t(&fa_)[MBM], bf16x8_t(&fb_)[MBN], int nr, int nv) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < MBM; ++i)
 #pragma unroll
       for (int j = 0; j < MBN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_[i], fb_[j], acc[i][j], 0, 0, 0);
-    constexpr int NR = MBM + MBN, NM = MBM * MBN;
+    constexpr int NM = MBM * MBN;
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       if (i < nv) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
   };
+  // wait until stage `kt + 1` has landed: the newer NST - 2 stages' loads may still fly
+  auto wait_next = [&]() __attribute__((always_inline)) {
+    if (NST == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (NST == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::NV) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 2) * C::NV) : "memory");
+  };
+  constexpr int NR = MBM + MBN;
+
   const int nk = (int)(K / BK);
-  dma_p(0, 0);
-  dma_q(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int s0 = 0; s0 < NST - 1; ++s0) {
+    const int k0 = (s0 < nk ? s0 : nk - 1) * BK;
+    dma_p(s0, k0);
+    dma_q(s0, k0);
+  }
+  wait_next();
   __syncthreads();
   ldfrag(smem, 0, fa0, fb0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    // the last step reloads its own K slice into the idle stage (never read),
-    // so no branch splits the body: each slice's MFMAs interleave with the next
-    // slice's fragment reads and with half the next stage's buffer loads
-    const int kn = (kt + 1 < nk ? kt + 1 : kt) * BK;
-    const char *sa = smem + st * C::STAGE;
-    dma_p(st ^ 1, kn);
-    ldfrag(sa, 1, fa1, fb1);
-    mma(fa0, fb0, C::NIA);
-    __builtin_amdgcn_sched_barrier(0);
-    dma_q(st ^ 1, kn);
-    ldfrag(sa, 2, fa0, fb0);
-    mma(fa1, fb1, C::NIB);
-    __builtin_amdgcn_sched_barrier(0);
-    ldfrag(sa, 3, fa1, fb1);
-    mma(fa0, fb0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    const char *sa = smem + (kt % NST) * C::STAGE;
+    // the next load goes into the stage consumed one step ago; near the end it
+    // reloads the last K slice into a stage nobody reads again, so the body has
+    // no branch and the loads interleave with the MFMAs
+    const int tgt = (kt + NST - 1) % NST;
+    const int kn = (kt + NST - 1 < nk ? kt + NST - 1 : nk - 1) * BK;
+    if (C::KS == 4) {
+      dma_p(tgt, kn);
+      ldfrag(sa, 1, fa1, fb1);
+      mma(fa0, fb0, NR, C::NIA);
+      __builtin_amdgcn_sched_barrier(0);
+      dma_q(tgt, kn);
+      ldfrag(sa, 2, fa0, fb0);
+      mma(fa1, fb1, NR, C::NIB);
+      __builtin_amdgcn_sched_barrier(0);
+      ldfrag(sa, 3, fa1, fb1);
+      mma(fa0, fb0, NR, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      dma_p(tgt, kn);
+      dma_q(tgt, kn);
+      ldfrag(sa, 1, fa1, fb1);
+      mma(fa0, fb0, NR, C::NV);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (CAPD) {
       const int mb = kt * BK - dk0;                  // tile row held at K offset 0 of this stage
       if (mb >= 0 && mb < C::TM) {
@@ -205,8 +232,8 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
 #pragma unroll
               for (int g4 = 0; g4 < 4; ++g4) {
                 const int kl = bm - mb + g4 * 8 + (lane >> 5) * 4;
-                const uint2 d = *reinterpret_cast<const uint2 *>(sa + C::SEGA + n * 128 +
-                                                                 (((kl >> 3) ^ swz(lrow)) << 4) + (kl & 7) * 2);
+                const uint2 d = *reinterpret_cast<const uint2 *>(sa + C::SEGA + n * RB +
+                                                                 (((kl >> 3) ^ swz<BK>(lrow)) << 4) + (kl & 7) * 2);
                 acc[i][j][g4 * 4 + 0] = fmaf(dscale, __uint_as_float(d.x << 16), acc[i][j][g4 * 4 + 0]);
                 acc[i][j][g4 * 4 + 1] = fmaf(dscale, __uint_as_float(d.x & 0xFFFF0000u), acc[i][j][g4 * 4 + 1]);
                 acc[i][j][g4 * 4 + 2] = fmaf(dscale, __uint_as_float(d.y << 16), acc[i][j][g4 * 4 + 2]);
@@ -217,10 +244,14 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
         }
       }
     }
+    wait_next();
+    __syncthreads();
+    ldfrag(smem + ((kt + 1) % NST) * C::STAGE, 0, fa0, fb0);   // after the last step: unused
+    mma(fa1, fb1, NR, 0);
+  }
+  if (NST > 2) {                                 // trailing reloads land before the caller reuses the LDS
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    ldfrag(smem + (st ^ 1) * C::STAGE, 0, fa0, fb0);   // after the last step: unused
-    mma(fa1, fb1, 0);
   }
 }
 

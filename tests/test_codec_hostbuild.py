@@ -146,3 +146,44 @@ def test_xcd_tile_map_is_an_in_bounds_bijection(tmp_path):
             seen = np.zeros(m * n, np.int32)
             assert L.check(m, n, seen.ctypes.data) == 0, (m, n)
             assert np.all(seen == 1), (m, n)
+
+
+SWZ_SHIM = r"""
+#include "lds_swizzle.h"
+int swz64(int r) { return lds_swz<64>(r); }
+int swz32(int r) { return lds_swz<32>(r); }
+"""
+
+
+def test_lds_swizzle_conflict_free_and_load_consistent(tmp_path):
+    """The contraction's LDS chunk swizzle (csrc/lds_swizzle.h), compiled for the
+    host: (1) a fragment read -- lanes 0..31 on 32 consecutive rows, lanes 32..63
+    on the next logical chunk -- puts every aligned group of 8 and of 16 lanes on
+    distinct 16-byte bank groups (256- and 128-byte-per-cycle LDS models);
+    (2) the swizzle repeats with the rows one buffer load spans, so a load's
+    per-lane chunk pattern is the same for every row block it fills."""
+    src = tmp_path / "swz.cpp"
+    src.write_text(SWZ_SHIM.replace("int swz", 'extern "C" int swz'))
+    so = tmp_path / "swz.so"
+    subprocess.run(["g++", "-O1", "-shared", "-fPIC", "-I", CSRC, str(src), "-o", str(so)], check=True)
+    L = ctypes.CDLL(str(so))
+    for bk, fn in ((64, L.swz64), (32, L.swz32)):
+        cpr, rb = bk // 8, bk * 2
+        for base in range(0, 256, 32):
+            for c in range(0, cpr, 2):
+                addr = []
+                for lane in range(64):
+                    r = base + (lane & 31)
+                    logical = c + (lane >> 5)
+                    addr.append(r * rb + (logical ^ fn(r)) * 16)
+                for g, mod in ((16, 16), (8, 8)):
+                    for s0 in range(0, 64, g):
+                        banks = [(a // 16) % mod for a in addr[s0:s0 + g]]
+                        assert len(set(banks)) == g, (bk, base, c, s0, banks)
+        rpi = 1024 // rb
+        for nw in (4, 8):
+            for r in range(rpi * nw):
+                for i in range(1, 8):
+                    assert fn(r) == fn(r + rpi * nw * i), (bk, nw, r, i)
+        for r in range(64):                          # each row's chunks stay a permutation
+            assert sorted(c ^ fn(r) for c in range(cpr)) == list(range(cpr))
