@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SSHDP_ABI_VERSION 1
+#define SSHDP_ABI_VERSION 2
 
 /* Status codes.  The planning errors are the rejections of [SS-HSDP Appendix A,
  * Table 4]: incompatible metadata, invalid geometry, storage overlap. */
@@ -99,18 +99,23 @@ enum {
  * rows `row_stride` elements apart) at `offset` elements from its parent's first
  * element.  A 1-D tensor is rows = 1.  `is_unit` marks an update parameter (a
  * leaf of the optimisation [SS-HSDP §3.1]) with `optimizer` SSHDP_OPT_MUON or
- * SSHDP_OPT_ADAMW; `quantize` marks a region (a runtime weight, or a unit) that
- * G requantises to MXFP8.  Rules (else the error named):
+ * SSHDP_OPT_ADAMW; `quantize` marks a region (a runtime weight, or a unit)
+ * that G turns into its runtime form [SS-HSDP §2.1: G casts or quantises the
+ * main weight]: SSHDP_G_MXFP8 requantises it to MXFP8 (codes + scales),
+ * SSHDP_G_BF16 casts it to bfloat16 (w_bf16).  Rules (else the error named):
  *   parent is -1 or an earlier node index                          (TREE)
  *   rows, cols >= 1, offset >= 0, row_stride >= cols if rows > 1   (SCHEMA)
  *   the view lies inside its parent's extent and the root           (BOUNDS)
  *   a Muon unit is 2-D (rows, cols >= 2) and its first element, row_stride
  *     and cols are multiples of 4 (16-byte vectors)                (SCHEMA)
- *   a quantised region is contiguous (row_stride == cols), with cols and its
+ *   quantize is SSHDP_G_NONE, SSHDP_G_MXFP8 or SSHDP_G_BF16          (SCHEMA)
+ *   an MXFP8 region is contiguous (row_stride == cols), with cols and its
  *     first element multiples of 32; for TILE32X4 also rows % 32 == 0 and
  *     cols % 128 == 0; for BLOCK32X32 also rows % 32 == 0 and the
  *     first element a multiple of 1024                              (SCHEMA)
- *   units are pairwise disjoint; quantised regions too             (OVERLAP)
+ *   a BF16 region is contiguous, with cols and its first element
+ *     multiples of 8 (16-byte stores)                               (SCHEMA)
+ *   units are pairwise disjoint; G regions (both kinds) too        (OVERLAP)
  * Checks run node by node in index order; overlap is checked last. */
 typedef struct {
   int32_t parent;
@@ -122,6 +127,8 @@ typedef struct {
   int32_t optimizer;
   int32_t quantize;
 } sshdp_node;
+
+enum { SSHDP_G_NONE = 0, SSHDP_G_MXFP8 = 1, SSHDP_G_BF16 = 2 };
 
 /* Plan options.  Defaults (sshdp_default_opts): 5 Newton-Schulz steps with
  * (a, b, c) = (3.4445, -4.7750, 2.0315) on the Frobenius-normalised u, ns_eps =
@@ -150,8 +157,10 @@ typedef struct { float lr, beta1, beta2, eps, weight_decay; } sshdp_adamw_hp;
  * w_main, grad, mom (Muon momentum and AdamW first moment): fp32, root_numel
  * elements.  adam_v: fp32 root or NULL when the plan has no AdamW units.
  * codes: uint8 root of root_numel bytes (E4M3FN).  scales: uint8, at least
- * sshdp_plan_stats.scale_bytes bytes (E8M0).  Only unit elements of w_main,
- * mom, adam_v and quantised-region bytes of codes/scales are written. */
+ * sshdp_plan_stats.scale_bytes bytes (E8M0).  w_bf16: bfloat16 root of
+ * root_numel elements, or NULL when the plan has no BF16 regions.  Only unit
+ * elements of w_main, mom, adam_v, MXFP8-region bytes of codes/scales and
+ * BF16-region elements of w_bf16 are written. */
 typedef struct {
   float *w_main;
   const float *grad;
@@ -159,6 +168,7 @@ typedef struct {
   float *adam_v;
   uint8_t *codes;
   uint8_t *scales;
+  uint16_t *w_bf16;
 } sshdp_buffers;
 
 typedef struct sshdp_plan sshdp_plan;   /* opaque; owns host tables and one device table block */
@@ -170,11 +180,14 @@ typedef struct {
   int64_t workspace_bytes;    /* device workspace sshdp_update_muon/_step need (256-aligned) */
   int32_t n_nodes, n_units, n_muon_units, n_adamw_units, n_quant_regions, n_groups;
   int64_t muon_elems, adamw_elems, quant_elems;
-  int64_t fused_quant_elems;  /* quantised elements G handles inside the AdamW pass       */
+  int64_t fused_quant_elems;  /* MXFP8 elements G handles inside the AdamW pass           */
   double ns_flops;            /* steps*(4 r^2 c + 2 r^3) summed over Muon units: the dense count */
   double ns_tile_flops;       /* MFMA flops the tile schedule executes per step (symmetric Gram and
                                  poly computed as tm <= tn tiles; padding to the tile included; units
                                  whose momentum is all zero skip theirs at run time)             */
+  int64_t cast_elems;         /* elements of BF16 regions                                  */
+  int32_t n_cast_regions;
+  int32_t pad_;
 } sshdp_plan_stats;
 
 /* One Newton-Schulz batch: the Muon units sharing an oriented shape r x c
@@ -227,10 +240,15 @@ int sshdp_update_adamw(const sshdp_plan *plan, const sshdp_buffers *bufs, const 
 int sshdp_requant_mxfp8(const sshdp_plan *plan, const float *w_main, uint8_t *codes, uint8_t *scales,
                         void *stream);
 
+/* G for every BF16 region [SS-HSDP §2.1]: w_bf16 = bfloat16(w_main), round to
+ * nearest even, at the elements' own offsets (a runtime view of a BF16 weight
+ * is the same sub-range of w_bf16).  Reads w_main; writes w_bf16. */
+int sshdp_cast_bf16(const sshdp_plan *plan, const float *w_main, uint16_t *w_bf16, void *stream);
+
 /* The whole update phase in order [SS-HSDP §3.4 "Update"]: Muon F, AdamW F
- * (fused with G for quantised regions holding only AdamW units), then G for the
- * remaining quantised regions.  Equivalent to sshdp_update_muon;
- * sshdp_update_adamw; sshdp_requant_mxfp8. */
+ * (fused with G for MXFP8 regions holding only AdamW units), then G for the
+ * remaining MXFP8 regions and the BF16 regions.  Equivalent to
+ * sshdp_update_muon; sshdp_update_adamw; sshdp_requant_mxfp8; sshdp_cast_bf16. */
 int sshdp_update_step(const sshdp_plan *plan, const sshdp_buffers *bufs, const sshdp_muon_hp *mh,
                       const sshdp_adamw_hp *ah, int64_t step, void *workspace, size_t workspace_bytes,
                       void *stream);
@@ -252,8 +270,8 @@ int sshdp_gemm_bf16_nt(const void *P, const void *Q, const void *D, void *O, voi
  * 4 NS update (+f2), 5 AdamW, 6 AdamW+G fused, 7 G requant, 8 the whole
  * Newton-Schulz phase on the caller's stream (fork to join: NS launches of
  * different groups run concurrently on plan-owned streams, so classes 2-4 can
- * overlap in time).  Not thread-safe; for measurement only. */
-enum { SSHDP_PROF_CLASSES = 9 };
+ * overlap in time), 9 G bf16 cast.  Not thread-safe; for measurement only. */
+enum { SSHDP_PROF_CLASSES = 10 };
 int sshdp_profile_enable(sshdp_plan *plan, int32_t enable);
 int sshdp_profile_read(sshdp_plan *plan, double *ms, int64_t *launches);
 

@@ -23,7 +23,9 @@ OPT = {None: 0, "muon": 1, "adamw": 2}
 LAYOUT = {"rowmajor": 0, "tile32x4": 1, "block32x32": 2}
 PLAN_HOST_ONLY = 1
 PROF_CLASSES = ["momentum", "norm", "ns_gram", "ns_poly", "ns_update", "adamw", "adamw_requant", "requant",
-                "ns_phase"]
+                "ns_phase", "cast_bf16"]
+# node["quantize"]: False/None (no G), True or "mxfp8" (MXFP8 codes + scales), "bf16" (bfloat16 cast)
+GMODE = {None: 0, False: 0, True: 1, "mxfp8": 1, "bf16": 2}
 
 
 class SshdpError(RuntimeError):
@@ -56,7 +58,8 @@ class AdamWHP(ctypes.Structure):
 
 class Buffers(ctypes.Structure):
     _fields_ = [("w_main", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("mom", ctypes.c_void_p),
-                ("adam_v", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+                ("adam_v", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("w_bf16", ctypes.c_void_p)]
 
 
 class PlanStats(ctypes.Structure):
@@ -66,7 +69,8 @@ class PlanStats(ctypes.Structure):
                 ("n_quant_regions", ctypes.c_int32), ("n_groups", ctypes.c_int32),
                 ("muon_elems", ctypes.c_int64), ("adamw_elems", ctypes.c_int64), ("quant_elems", ctypes.c_int64),
                 ("fused_quant_elems", ctypes.c_int64), ("ns_flops", ctypes.c_double),
-                ("ns_tile_flops", ctypes.c_double)]
+                ("ns_tile_flops", ctypes.c_double), ("cast_elems", ctypes.c_int64), ("n_cast_regions", ctypes.c_int32),
+                ("pad_", ctypes.c_int32)]
 
 
 class GroupInfo(ctypes.Structure):
@@ -93,6 +97,7 @@ SIGNATURES = {
     "sshdp_update_adamw": ([_P, ctypes.POINTER(Buffers), ctypes.POINTER(AdamWHP), ctypes.c_int64, _P],
                            ctypes.c_int),
     "sshdp_requant_mxfp8": ([_P, _P, _P, _P, _P], ctypes.c_int),
+    "sshdp_cast_bf16": ([_P, _P, _P, _P], ctypes.c_int),
     "sshdp_update_step": ([_P, ctypes.POINTER(Buffers), ctypes.POINTER(MuonHP), ctypes.POINTER(AdamWHP),
                            ctypes.c_int64, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "sshdp_gemm_bf16_nt": ([_P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -153,12 +158,19 @@ def default_opts():
     return o
 
 
+def _gmode(q):
+    try:
+        return GMODE[q]
+    except (KeyError, TypeError):
+        return int(q) if isinstance(q, int) else 99
+
+
 def node_array(nodes):
     arr = (Node * len(nodes))()
     for i, n in enumerate(nodes):
         arr[i] = Node(int(n["parent"]), int(bool(n["is_unit"])), int(n["offset"]), int(n["rows"]),
                       int(n["cols"]), int(n["row_stride"]), OPT.get(n.get("optimizer"), 99),
-                      int(bool(n.get("quantize"))))
+                      _gmode(n.get("quantize")))
     return arr
 
 
@@ -225,8 +237,8 @@ class Plan:
             pass
 
 
-def buffers(w_main=None, grad=None, mom=None, adam_v=None, codes=None, scales=None):
-    return Buffers(_ptr(w_main), _ptr(grad), _ptr(mom), _ptr(adam_v), _ptr(codes), _ptr(scales))
+def buffers(w_main=None, grad=None, mom=None, adam_v=None, codes=None, scales=None, w_bf16=None):
+    return Buffers(_ptr(w_main), _ptr(grad), _ptr(mom), _ptr(adam_v), _ptr(codes), _ptr(scales), _ptr(w_bf16))
 
 
 def muon_hp(lr=0.02, momentum=0.95, weight_decay=0.0):
@@ -250,6 +262,10 @@ def update_adamw(plan, bufs, hp, step, stream=None):
 def requant_mxfp8(plan, w_main, codes, scales, stream=None):
     _check(lib().sshdp_requant_mxfp8(plan.handle, _ptr(w_main), _ptr(codes), _ptr(scales), _stream(stream)),
            "sshdp_requant_mxfp8")
+
+
+def cast_bf16(plan, w_main, w_bf16, stream=None):
+    _check(lib().sshdp_cast_bf16(plan.handle, _ptr(w_main), _ptr(w_bf16), _stream(stream)), "sshdp_cast_bf16")
 
 
 def update_step(plan, bufs, mhp, ahp, step, workspace, workspace_bytes, stream=None):

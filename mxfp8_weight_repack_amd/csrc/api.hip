@@ -160,6 +160,17 @@ int sshdp_requant_mxfp8(const sshdp_plan *p, const float *w_main, uint8_t *codes
   return hip_status(launch_quant(*p, 0, (int64_t)p->qchunks.size(), false, b, nullptr, 1, s));
 }
 
+int sshdp_cast_bf16(const sshdp_plan *p, const float *w_main, uint16_t *w_bf16, void *stream) {
+  int st = check_plan(p);
+  if (st != SSHDP_OK) return st;
+  if (p->cchunks.empty()) return SSHDP_OK;
+  if (!w_main || !w_bf16) return SSHDP_ERR_ARG;
+  if (!aligned16(w_main) || !aligned16(w_bf16)) return SSHDP_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Prof pr(p, 9, s);
+  return hip_status(launch_cast_bf16(*p, w_main, w_bf16, s));
+}
+
 int sshdp_update_step(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_muon_hp *mh,
                       const sshdp_adamw_hp *ah, int64_t step, void *ws, size_t ws_bytes, void *stream) {
   int st = check_plan(p);
@@ -176,6 +187,10 @@ int sshdp_update_step(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_m
   if (!p->qchunks.empty() || !p->q32tiles.empty()) {
     st = check_quant(b->w_main, b->codes, b->scales);
     if (st != SSHDP_OK) return st;
+  }
+  if (!p->cchunks.empty()) {
+    if (!b->w_main || !b->w_bf16) return SSHDP_ERR_ARG;
+    if (!aligned16(b->w_main) || !aligned16(b->w_bf16)) return SSHDP_ERR_ALIGN;
   }
   if (!p->munits.empty()) {
     st = run_muon(p, b, mh, ws, ws_bytes, s);
@@ -200,6 +215,11 @@ int sshdp_update_step(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_m
   if (!p->q32tiles.empty()) {
     Prof pr(p, 7, s);
     st = hip_status(launch_quant32(*p, b->w_main, b->codes, b->scales, s));
+  }
+  if (st != SSHDP_OK) return st;
+  if (!p->cchunks.empty()) {
+    Prof pr(p, 9, s);
+    st = hip_status(launch_cast_bf16(*p, b->w_main, b->w_bf16, s));
   }
   return st;
 }

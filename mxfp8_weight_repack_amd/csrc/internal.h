@@ -94,6 +94,13 @@ struct Q32Tile {
   int32_t nb;           // blocks in this tile (1..4)
 };
 
+// BF16-cast work item: elements [base, base + n) of one region (n <= kChunk, n % 8 == 0).
+struct CChunk {
+  int64_t base;
+  int32_t n;
+  int32_t pad_;
+};
+
 struct DeviceTables {
   MuonUnit *munits = nullptr;
   F0Tile *f0tiles = nullptr;
@@ -102,6 +109,7 @@ struct DeviceTables {
   QRegion *qregions = nullptr;
   QChunk *qchunks = nullptr;
   Q32Tile *q32tiles = nullptr;
+  CChunk *cchunks = nullptr;
   NsGroupDev *ns_groups = nullptr;
   NsTile *ns_tiles[kMaxLanes][3][2] = {};   // [lane][stage: Gram, poly, update][tile: 128, 256]
 };
@@ -129,6 +137,7 @@ struct sshdp_plan {
   std::vector<sshdp::QChunk> qchunks;   // fused-eligible chunks first
   int64_t n_qchunks_fused = 0;
   std::vector<sshdp::Q32Tile> q32tiles; // BLOCK32X32 layout: all requant work
+  std::vector<sshdp::CChunk> cchunks;   // BF16 regions
   size_t ws_uscale = 0, ws_partials = 0, ws_bytes = 0;
   sshdp_plan_stats stats{};
   bool host_only = true;
@@ -158,4 +167,5 @@ hipError_t launch_adamw(const ASeg *segs, int64_t nseg, const sshdp_buffers &b, 
 hipError_t launch_quant(const sshdp_plan &p, int64_t first, int64_t count, bool fused, const sshdp_buffers &b,
                         const sshdp_adamw_hp *hp, int64_t step, hipStream_t s);
 hipError_t launch_quant32(const sshdp_plan &p, const float *w, uint8_t *codes, uint8_t *scales, hipStream_t s);
+hipError_t launch_cast_bf16(const sshdp_plan &p, const float *w, uint16_t *out, hipStream_t s);
 }  // namespace sshdp

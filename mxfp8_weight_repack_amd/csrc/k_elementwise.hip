@@ -27,6 +27,17 @@ namespace {
 __device__ __forceinline__ uint32_t fbits(float x) { return __float_as_uint(x); }
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bfloat16 (a in the low half), v_cvt_pk_bf16_f32: round
+// to nearest even, identical to mx_bf16_bits for every non-NaN float32
+// (checked exhaustively on the device).
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 
 // streaming load that is not kept in the caches (read-once data)
 __device__ __forceinline__ float4 load_nt(const float *p) {
@@ -358,6 +369,36 @@ __global__ __launch_bounds__(256) void k_quant32(const Q32Tile *__restrict__ til
   if (rg == 0 && (c4 & 7) == 0) scales[q.sidx + blk] = (uint8_t)sb;
 }
 
+// G as a bfloat16 cast: one chunk (<= kChunk elements, a multiple of 8) per
+// workgroup, two passes of 2048; a lane converts 8 consecutive elements
+// (v_cvt_pk_bf16_f32, round to nearest even) and stores 16 bytes.
+__global__ __launch_bounds__(256) void k_cast_bf16(const CChunk *__restrict__ chunks, const float *__restrict__ w,
+                                                   uint16_t *__restrict__ out) {
+  const CChunk q = chunks[blockIdx.x];
+  const int t = threadIdx.x;
+  float4 a[2], b[2];
+  bool live[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int off = p * 2048 + 8 * t;
+    live[p] = off < q.n;
+    if (live[p]) {
+      a[p] = *reinterpret_cast<const float4 *>(w + q.base + off);
+      b[p] = *reinterpret_cast<const float4 *>(w + q.base + off + 4);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    if (!live[p]) continue;
+    u32x4_t h;
+    h.x = pk_bf16(a[p].x, a[p].y);
+    h.y = pk_bf16(a[p].z, a[p].w);
+    h.z = pk_bf16(b[p].x, b[p].y);
+    h.w = pk_bf16(b[p].z, b[p].w);
+    __builtin_nontemporal_store(h, reinterpret_cast<u32x4_t *>(out + q.base + p * 2048 + 8 * t));
+  }
+}
+
 AdamConst adam_const(const sshdp_adamw_hp &hp, int64_t step) {
   AdamConst c;
   c.b1 = hp.beta1;
@@ -420,6 +461,15 @@ hipError_t launch_quant32(const sshdp_plan &p, const float *w, uint8_t *codes, u
   for (int64_t first = 0; first < n; first += 0x7FFFFFFF) {
     const int64_t cnt = std::min<int64_t>(n - first, 0x7FFFFFFF);
     hipLaunchKernelGGL(k_quant32, dim3((unsigned)cnt), dim3(256), 0, s, p.d.q32tiles + first, w, codes, scales);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_bf16(const sshdp_plan &p, const float *w, uint16_t *out, hipStream_t s) {
+  const int64_t n = (int64_t)p.cchunks.size();
+  for (int64_t first = 0; first < n; first += 0x7FFFFFFF) {
+    const int64_t cnt = std::min<int64_t>(n - first, 0x7FFFFFFF);
+    hipLaunchKernelGGL(k_cast_bf16, dim3((unsigned)cnt), dim3(256), 0, s, p.d.cchunks + first, w, out);
   }
   return hipGetLastError();
 }

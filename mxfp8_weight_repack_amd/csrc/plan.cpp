@@ -68,7 +68,12 @@ int validate(const sshdp_node *nodes, int32_t n, int64_t root_numel, int layout,
       if (a % 4 || rs % 4 || nd.cols % 4) return SSHDP_ERR_SCHEMA;
       if (nd.rows > (1 << 30) || nd.cols > (1 << 30)) return SSHDP_ERR_SCHEMA;
     }
-    if (nd.quantize) {
+    if (nd.quantize != SSHDP_G_NONE && nd.quantize != SSHDP_G_MXFP8 && nd.quantize != SSHDP_G_BF16)
+      return SSHDP_ERR_SCHEMA;
+    if (nd.quantize == SSHDP_G_BF16) {
+      if (rs != nd.cols || nd.cols % 8 || a % 8 || nd.cols > (1 << 30)) return SSHDP_ERR_SCHEMA;
+    }
+    if (nd.quantize == SSHDP_G_MXFP8) {
       if (rs != nd.cols || nd.cols % 32 || a % 32) return SSHDP_ERR_SCHEMA;
       if (layout == SSHDP_SCALE_TILE32X4 && (nd.rows % 32 || nd.cols % 128)) return SSHDP_ERR_SCHEMA;
       if (layout == SSHDP_SCALE_BLOCK32X32 && (nd.rows % 32 || a % 1024)) return SSHDP_ERR_SCHEMA;
@@ -85,7 +90,7 @@ int validate(const sshdp_node *nodes, int32_t n, int64_t root_numel, int layout,
   }
   if (any_overlap(units)) return SSHDP_ERR_OVERLAP;
   for (int32_t i = 0; i < n; ++i)
-    if (nodes[i].quantize) quant.push_back({abs[i], nodes[i].rows * nodes[i].cols, 0, i});
+    if (nodes[i].quantize != SSHDP_G_NONE) quant.push_back({abs[i], nodes[i].rows * nodes[i].cols, 0, i});
   if (any_overlap(quant)) return SSHDP_ERR_OVERLAP;
   return SSHDP_OK;
 }
@@ -302,7 +307,15 @@ void build_elementwise(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
   std::vector<QChunk> fused, plain;
   for (int32_t i = 0; i < n; ++i) {
     const sshdp_node &nd = nodes[i];
-    if (!nd.quantize) continue;
+    if (nd.quantize == SSHDP_G_BF16) {
+      const int64_t a = p.node_abs[i], len = nd.rows * nd.cols;
+      for (int64_t pos = a; pos < a + len; pos += kChunk)
+        p.cchunks.push_back({pos, (int32_t)std::min<int64_t>(kChunk, a + len - pos), 0});
+      p.stats.cast_elems += len;
+      p.stats.n_cast_regions++;
+      continue;
+    }
+    if (nd.quantize != SSHDP_G_MXFP8) continue;
     const int32_t ri = (int32_t)p.qregions.size();
     const int64_t a = p.node_abs[i], len = nd.rows * nd.cols;
     p.qregions.push_back({a, nd.rows, (int32_t)nd.cols, 0});
@@ -392,7 +405,7 @@ size_t table_bytes(const std::vector<T> &v) { return round_up((int64_t)(v.size()
 int upload(sshdp_plan &p) {
   const size_t total = table_bytes(p.munits) + table_bytes(p.f0tiles) + table_bytes(p.aseg_all) +
                        table_bytes(p.aseg_unfused) + table_bytes(p.qregions) + table_bytes(p.qchunks) +
-                       table_bytes(p.q32tiles) + table_bytes(p.ns_groups) + 256;
+                       table_bytes(p.q32tiles) + table_bytes(p.cchunks) + table_bytes(p.ns_groups) + 256;
   size_t tiles_total = 0;
   for (auto &ln : p.ns_tiles)
     for (auto &st : ln)
@@ -415,6 +428,7 @@ int upload(sshdp_plan &p) {
   put(p.qregions, p.d.qregions);
   put(p.qchunks, p.d.qchunks);
   put(p.q32tiles, p.d.q32tiles);
+  put(p.cchunks, p.d.cchunks);
   put(p.ns_groups, p.d.ns_groups);
   for (int ln = 0; ln < kMaxLanes; ++ln)
     for (int st = 0; st < 3; ++st)

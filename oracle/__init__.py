@@ -32,7 +32,7 @@ each function's docstring.  Parity status of each part:
 
 from .views import ViewError, resolve_views, unit_indices
 from .numerics import bf16_rne, e4m3_decode_table, e4m3_encode, e4m3_decode, e8m0_exponent
-from .mxfp8 import quantize_blocks, quantize_blocks_32x32, scale_index, requant_root
+from .mxfp8 import quantize_blocks, quantize_blocks_32x32, scale_index, requant_root, cast_root_bf16
 from .muon import momentum_step, newton_schulz, muon_scale, muon_update_unit
 from .adamw import adamw_step
 from .step import update_step, OracleHyper
@@ -40,7 +40,7 @@ from .step import update_step, OracleHyper
 __all__ = [
     "ViewError", "resolve_views", "unit_indices",
     "bf16_rne", "e4m3_decode_table", "e4m3_encode", "e4m3_decode", "e8m0_exponent",
-    "quantize_blocks", "quantize_blocks_32x32", "scale_index", "requant_root",
+    "quantize_blocks", "quantize_blocks_32x32", "scale_index", "requant_root", "cast_root_bf16",
     "momentum_step", "newton_schulz", "muon_scale", "muon_update_unit",
     "adamw_step", "update_step", "OracleHyper",
 ]

@@ -34,7 +34,7 @@ transposed operand: the blocks of X^T are the transposes of X's.
 
 import numpy as np
 
-from .numerics import e4m3_encode, e8m0_exponent
+from .numerics import bf16_rne, e4m3_encode, e8m0_exponent
 from .views import unit_indices
 
 
@@ -147,3 +147,17 @@ def requant_root(w_root, resolved, layout, codes_root, scales_root, fast=True):
         codes_root[idx] = c
         scales_root[scale_index(layout, r["abs"], r["rows"], r["cols"])] = s
     return codes_root, scales_root
+
+
+def cast_root_bf16(w_root, resolved, out_root):
+    """G as a bfloat16 cast [SS-HSDP §2.1] over every 'bf16' region of a
+    resolved view table: out_root (uint16, one per element of the fp32 root)
+    receives the bit pattern of bf16_rne(w) at the elements' own offsets;
+    other elements are left untouched."""
+    for r in resolved:
+        if not r.get("cast"):
+            continue
+        idx = unit_indices(r)
+        b = bf16_rne(np.asarray(w_root[idx], dtype=np.float32))
+        out_root[idx] = (b.view(np.uint32) >> 16).astype(np.uint16)
+    return out_root

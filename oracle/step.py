@@ -15,7 +15,7 @@ import numpy as np
 from .views import resolve_views, unit_indices
 from .muon import muon_update_unit
 from .adamw import adamw_step
-from .mxfp8 import requant_root
+from .mxfp8 import cast_root_bf16, requant_root
 
 
 @dataclass
@@ -41,9 +41,10 @@ class OracleHyper:
 
 def update_step(nodes, root_numel, w, g, m, v, codes, scales, step, hp=None,
                 layout="rowmajor", do_muon=True, do_adamw=True, do_requant=True,
-                keep_v=False):
-    """Apply one step in place to float32 roots w, m, v and uint8 roots codes,
-    scales.  Returns a dict {unit index: float64 NS direction} if keep_v."""
+                keep_v=False, bf16_root=None):
+    """Apply one step in place to float32 roots w, m, v, uint8 roots codes,
+    scales and (when given) the uint16 root of bf16-cast regions.  Returns a
+    dict {unit index: float64 NS direction} if keep_v."""
     hp = hp or OracleHyper()
     res = resolve_views(nodes, root_numel, layout)
     dirs = {}
@@ -64,4 +65,6 @@ def update_step(nodes, root_numel, w, g, m, v, codes, scales, step, hp=None,
             w[idx], m[idx], v[idx] = w_new, m_new, v_new
     if do_requant:
         requant_root(w, res, layout, codes, scales)
+        if bf16_root is not None:
+            cast_root_bf16(w, res, bf16_root)
     return dirs

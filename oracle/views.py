@@ -15,7 +15,10 @@ A node is a mapping with keys
   row_stride  elements between consecutive rows (== cols when contiguous)
   is_unit     True for an update parameter (leaf of the optimisation)
   optimizer   'muon' or 'adamw' for units, None otherwise
-  quantize    True if this region is requantised to MXFP8 by G
+  quantize    G mode of a region [SS-HSDP §2.1: G casts or quantises the main
+              weight]: True (or 'mxfp8') = requantised to MXFP8, 'bf16' = cast
+              to bfloat16, False/None = no G.  Resolved entries carry
+              ``quantize`` (MXFP8) and ``cast`` (bf16) as booleans.
 
 Reading taken where the pages are silent: the planner's error classes and their
 precedence (one rule list, first failing node in index order, overlap last) are
@@ -64,7 +67,13 @@ def resolve_views(nodes, root_numel, scale_layout="rowmajor"):
             raise ViewError("BOUNDS", f"node {i}: view leaves its parent")
         is_unit = bool(nd["is_unit"])
         opt = nd.get("optimizer")
-        q = bool(nd.get("quantize", False))
+        qv = nd.get("quantize", False)
+        if qv not in (None, False, True, "mxfp8", "bf16", 0, 1, 2):
+            raise ViewError("SCHEMA", f"node {i}: unknown G mode {qv!r}")
+        q = qv in (True, "mxfp8", 1)
+        cast = qv in ("bf16", 2)
+        if cast and (rs != cols or cols % 8 or a % 8):
+            raise ViewError("SCHEMA", f"node {i}: bf16 region not contiguous or not 8-aligned")
         if is_unit and opt not in ("muon", "adamw"):
             raise ViewError("SCHEMA", f"node {i}: unit without a known optimizer")
         if is_unit and opt == "muon":
@@ -81,13 +90,13 @@ def resolve_views(nodes, root_numel, scale_layout="rowmajor"):
                 raise ViewError("SCHEMA", f"node {i}: block32x32 needs rows%32==0 and a 1024-aligned start")
         r = dict(nd)
         r.update(abs=a, extent=ext, row_stride=rs, rows=rows, cols=cols,
-                 is_unit=is_unit, optimizer=opt if is_unit else None, quantize=q)
+                 is_unit=is_unit, optimizer=opt if is_unit else None, quantize=q, cast=cast)
         out.append(r)
     # storage overlap, by brute force marking [SS-HSDP Appendix A, Table 4]
-    for key, what in (("is_unit", "units"), ("quantize", "quantised regions")):
+    for key, what in (("is_unit", "units"), ("quantize", "G regions")):
         marks = np.zeros(root_numel, dtype=np.uint8)
         for r in out:
-            if not r[key]:
+            if not (r["quantize"] or r["cast"]) if key == "quantize" else not r[key]:
                 continue
             if r["row_stride"] == r["cols"]:
                 segs = [(r["abs"], r["rows"] * r["cols"])]

@@ -12,6 +12,8 @@ Gates (stated per test):
   untouched.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -212,6 +214,46 @@ def test_update_step_parity_block32x32(case):
     z = np.zeros_like(w0)
     ref, dirs = oracle_step(wl, "block32x32", w0, g, z, z, 1)
     check_step(wl, "block32x32", h, ref, dirs, w0)
+
+
+def test_bf16_cast_regions_in_the_step_and_alone():
+    """G as a bfloat16 cast: the O projection (Muon) and both norms (AdamW)
+    of the small dense block are bf16 regions, the rest MXFP8.  After the
+    step, the bf16 root equals the oracle's cast of the GPU-updated weights
+    bit for bit (and nothing outside the bf16 regions is written); updates and
+    MXFP8 bytes meet the usual gates; the cast entry alone matches too."""
+    from test_oracle_bf16_cast import bf16_variant
+    base = workloads.config(2, small=True)
+    wl = dataclasses.replace(base, name=base.name + " (bf16 regions)", nodes=bf16_variant(base))
+    say(f"bf16 cast {wl.name}")
+    w0, g = wl.arrays()
+    st = DeviceState(wl)
+    out = torch.full((wl.root_numel,), 0x1234, dtype=torch.int16, device="cuda")
+    bufs = sh.buffers(st.w, st.g, st.m, st.v, st.codes, st.scales, out)
+    sh.update_step(st.plan, bufs, sh.muon_hp(**MUON), sh.adamw_hp(**ADAM), 1, st.ws, st.ws_bytes, st.stream())
+    h = st.host()
+    got = out.cpu().numpy().view(np.uint16)
+    z = np.zeros_like(w0)
+    ref, dirs = oracle_step(wl, wl.scale_layout, w0, g, z, z, 1)
+    check_step(wl, wl.scale_layout, h, ref, dirs, w0)
+    exp = np.full(wl.root_numel, 0x1234, np.uint16)
+    res = resolve_views(wl.nodes, wl.root_numel, wl.scale_layout)
+    oracle.cast_root_bf16(h["w"], res, exp)
+    assert np.array_equal(got, exp)
+    # the cast entry alone, on planted specials
+    w = h["w"].copy()
+    a = [r for r in res if r["cast"]][0]["abs"]
+    w[a:a + 8] = [np.nan, np.inf, -np.inf, -0.0, 1e-41, 3.4e38, 1.00390625, -1.01171875]
+    wt = torch.from_numpy(w).cuda()
+    out.fill_(0x1234)
+    sh.cast_bf16(st.plan, wt, out, st.stream())
+    torch.cuda.synchronize()
+    exp = np.full(wl.root_numel, 0x1234, np.uint16)
+    oracle.cast_root_bf16(w, res, exp)
+    got = out.cpu().numpy().view(np.uint16)
+    nan = np.isnan(w)
+    assert np.array_equal(got[~nan], exp[~nan])
+    assert np.all((got[nan] & 0x7F80) == 0x7F80) and np.all((got[nan] & 0x7F) != 0)
 
 
 def test_update_step_equals_separate_calls_bitwise():
