@@ -43,6 +43,9 @@ def parse():
                     help="scale layout (default: the workload's own); block32x32 = one scale per 32x32 block")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=25.0, help="seconds of oracle work to aim for")
+    ap.add_argument("--part", choices=["step", "rs"], default="step",
+                    help="step: the update step (default); rs: the reduce-scatter tail on the workload's "
+                         "gradient size (4 BF16 slices -> BF16-SR partial; 2 partials accumulated into FP32)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="before timing, copy a 1 GiB buffer three times (a plain copy kernel of known "
                          "size, the calibration for HBM byte counters)")
@@ -118,6 +121,64 @@ def cpu_baseline(wl, budget_s):
             "seconds": dt}
 
 
+def bench_rs(args, wl):
+    """The reduce-scatter tail at the workload's gradient size: a local
+    reducer sums 4 BF16 slices into a BF16 partial with stochastic rounding
+    (10 B/element: 4 x 2 read, 2 written), then the final reduction adds 2
+    such partials into the persistent FP32 gradient (12 B/element).  A step is
+    one of each; inputs are resident before timing."""
+    import torch
+    import mxfp8_weight_repack_amd as sh
+    n = (wl.root_numel + 15) // 16 * 16
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev).manual_seed(args.config)
+    slices = [(torch.randn(n, device=dev, generator=gen) * 1e-3).to(torch.bfloat16) for _ in range(4)]
+    parts = [torch.empty(n, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    g = torch.zeros(n, dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream()
+    sp = s.cuda_stream
+
+    def step(t):
+        for i in range(2):
+            sh.rs_reduce(slices, "bf16", parts[i], "bf16_sr", n, seed=1234, ctr=2 * t + i, g0=0, stream=sp)
+        sh.rs_accumulate(parts, "bf16", g, n, first=(t == 0), stream=sp)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ms_red = ms_acc = 0.0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for t in range(args.steps):
+        ev[0].record(s)
+        for i in range(2):
+            sh.rs_reduce(slices, "bf16", parts[i], "bf16_sr", n, seed=1234, ctr=2 * t + i, g0=0, stream=sp)
+        ev[1].record(s)
+        sh.rs_accumulate(parts, "bf16", g, n, first=False, stream=sp)
+        ev[2].record(s)
+        torch.cuda.synchronize()
+        ms_red += ev[0].elapsed_time(ev[1]) / 2
+        ms_acc += ev[1].elapsed_time(ev[2])
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms_red /= args.steps
+    ms_acc /= args.steps
+    red_gbs = 10.0 * n / (ms_red / 1e3) / 1e9
+    acc_gbs = 12.0 * n / (ms_acc / 1e3) / 1e9
+    out = {"metric": "reduce-scatter tail GB/s (BF16-SR partial + FP32 accumulate)",
+           "value": (2 * 10.0 + 12.0) * n / ((2 * ms_red + ms_acc) / 1e3) / 1e9, "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": 2 * ms_red + ms_acc,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"{wl.name}: gradient of {n} elements, 4 BF16 slices per partial, 2 partials"},
+           "roofline": {"bound": "hbm", "kernel": "k_rs_reduce (BF16 in, BF16-SR out)", "achieved": red_gbs,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": red_gbs / HBM_PEAK_GBS, "traffic": None},
+           "accumulate_roofline": {"bound": "hbm", "kernel": "k_rs_accumulate", "achieved": acc_gbs,
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": acc_gbs / HBM_PEAK_GBS},
+           "components": {"rs_reduce": {"ms_per_call": ms_red}, "rs_accumulate": {"ms_per_call": ms_acc}}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -132,6 +193,8 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     wl = workloads.config(args.config)
+    if args.part == "rs":
+        return bench_rs(args, wl)
     w0, g0 = wl.arrays()
     layout = args.layout or wl.scale_layout
     plan = sh.Plan(wl.nodes, wl.root_numel, layout=layout)

@@ -245,6 +245,39 @@ int sshdp_requant_mxfp8(const sshdp_plan *plan, const float *w_main, uint8_t *co
  * is the same sub-range of w_bf16).  Reads w_main; writes w_bf16. */
 int sshdp_cast_bf16(const sshdp_plan *plan, const float *w_main, uint16_t *w_bf16, void *stream);
 
+/* The reduce-scatter tail [SS-HSDP §4.3 "Reduce-Scatter", Figure 5(e)]: within
+ * a node, the slices of one output partition arriving from several ranks are
+ * summed in FP32 by a local reducer; the partial stays FP32 or, for BF16
+ * gradients, is stored as BF16 with stochastic rounding; the final FP32
+ * reduction accumulates straight into the persistent gradient buffer (G'z2),
+ * with no result buffer and no separate addition pass.  On one GPU the slices
+ * are device buffers (what peer copies deliver).
+ *
+ * `inputs`: host array of n_inputs (1..8) device pointers, each n elements of
+ * in_dtype (SSHDP_RS_FP32 or SSHDP_RS_BF16), summed left to right, every
+ * addition rounded to FP32.  n % 16 == 0 and every pointer 16-byte aligned.
+ *
+ * sshdp_rs_reduce writes the sum to `out` as FP32 (SSHDP_RS_OUT_FP32) or as
+ * BF16 with stochastic rounding (SSHDP_RS_OUT_BF16_SR): the fp32 bit pattern
+ * plus a 16-bit random, truncated to its upper half (NaN kept), i.e. away from
+ * zero with probability (discarded bits)/2^16.  The randoms come from
+ * Philox4x64-10 [Salmon et al., SC 2011] with key (seed, 0): element j of the
+ * call is element g = g0 + j of the whole tensor (g0 % 16 == 0) and uses word
+ * (g/4) % 4, bits 16*(g%4), of the block at counter (g/16 + 1, ctr, 0, 0) --
+ * so a rank that restores (seed, ctr) reproduces its partials.
+ *
+ * sshdp_rs_accumulate: g = in_0 + in_1 + ... when `first` (the first
+ * microbatch initialises the buffer), else g = (g + in_0) + in_1 + ....
+ *
+ * Errors: ARG (null pointer, n_inputs out of range, n < 0, bad dtype/mode),
+ * SCHEMA (n or g0 not a multiple of 16), ALIGN. */
+enum { SSHDP_RS_FP32 = 0, SSHDP_RS_BF16 = 1 };
+enum { SSHDP_RS_OUT_FP32 = 0, SSHDP_RS_OUT_BF16_SR = 1 };
+int sshdp_rs_reduce(const void *const *inputs, int32_t n_inputs, int32_t in_dtype, void *out, int32_t out_mode,
+                    int64_t n, uint64_t seed, uint64_t ctr, int64_t g0, void *stream);
+int sshdp_rs_accumulate(const void *const *inputs, int32_t n_inputs, int32_t in_dtype, float *g, int64_t n,
+                        int32_t first, void *stream);
+
 /* The whole update phase in order [SS-HSDP §3.4 "Update"]: Muon F, AdamW F
  * (fused with G for MXFP8 regions holding only AdamW units), then G for the
  * remaining MXFP8 regions and the BF16 regions.  Equivalent to

@@ -98,6 +98,10 @@ SIGNATURES = {
                            ctypes.c_int),
     "sshdp_requant_mxfp8": ([_P, _P, _P, _P, _P], ctypes.c_int),
     "sshdp_cast_bf16": ([_P, _P, _P, _P], ctypes.c_int),
+    "sshdp_rs_reduce": ([_P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
+                         ctypes.c_uint64, ctypes.c_int64, _P], ctypes.c_int),
+    "sshdp_rs_accumulate": ([_P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int32, _P],
+                            ctypes.c_int),
     "sshdp_update_step": ([_P, ctypes.POINTER(Buffers), ctypes.POINTER(MuonHP), ctypes.POINTER(AdamWHP),
                            ctypes.c_int64, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "sshdp_gemm_bf16_nt": ([_P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -266,6 +270,27 @@ def requant_mxfp8(plan, w_main, codes, scales, stream=None):
 
 def cast_bf16(plan, w_main, w_bf16, stream=None):
     _check(lib().sshdp_cast_bf16(plan.handle, _ptr(w_main), _ptr(w_bf16), _stream(stream)), "sshdp_cast_bf16")
+
+
+RS_DTYPE = {"fp32": 0, "bf16": 1}
+RS_OUT = {"fp32": 0, "bf16_sr": 1}
+
+
+def _ptr_array(inputs):
+    arr = (ctypes.c_void_p * len(inputs))()
+    for k, t in enumerate(inputs):
+        arr[k] = _ptr(t)
+    return arr
+
+
+def rs_reduce(inputs, in_dtype, out, out_mode, n, seed=0, ctr=0, g0=0, stream=None):
+    _check(lib().sshdp_rs_reduce(_ptr_array(inputs), len(inputs), RS_DTYPE[in_dtype], _ptr(out), RS_OUT[out_mode],
+                                 int(n), int(seed), int(ctr), int(g0), _stream(stream)), "sshdp_rs_reduce")
+
+
+def rs_accumulate(inputs, in_dtype, g, n, first, stream=None):
+    _check(lib().sshdp_rs_accumulate(_ptr_array(inputs), len(inputs), RS_DTYPE[in_dtype], _ptr(g), int(n),
+                                     int(bool(first)), _stream(stream)), "sshdp_rs_accumulate")
 
 
 def update_step(plan, bufs, mhp, ahp, step, workspace, workspace_bytes, stream=None):

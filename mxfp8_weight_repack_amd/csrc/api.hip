@@ -171,6 +171,40 @@ int sshdp_cast_bf16(const sshdp_plan *p, const float *w_main, uint16_t *w_bf16, 
   return hip_status(launch_cast_bf16(*p, w_main, w_bf16, s));
 }
 
+namespace {
+int rs_check(const void *const *inputs, int32_t n_inputs, int32_t in_dtype, const void *out, int64_t n, int64_t g0) {
+  if (!inputs || !out || n_inputs < 1 || n_inputs > sshdp::kRsMaxInputs || n < 0) return SSHDP_ERR_ARG;
+  if (in_dtype != SSHDP_RS_FP32 && in_dtype != SSHDP_RS_BF16) return SSHDP_ERR_ARG;
+  for (int k = 0; k < n_inputs; ++k) {
+    if (!inputs[k]) return SSHDP_ERR_ARG;
+    if (!aligned16(inputs[k])) return SSHDP_ERR_ALIGN;
+  }
+  if (!aligned16(out)) return SSHDP_ERR_ALIGN;
+  if (n % 16 || g0 % 16 || g0 < 0) return SSHDP_ERR_SCHEMA;
+  return SSHDP_OK;
+}
+}  // namespace
+
+int sshdp_rs_reduce(const void *const *inputs, int32_t n_inputs, int32_t in_dtype, void *out, int32_t out_mode,
+                    int64_t n, uint64_t seed, uint64_t ctr, int64_t g0, void *stream) {
+  int st = rs_check(inputs, n_inputs, in_dtype, out, n, g0);
+  if (st != SSHDP_OK) return st;
+  if (out_mode != SSHDP_RS_OUT_FP32 && out_mode != SSHDP_RS_OUT_BF16_SR) return SSHDP_ERR_ARG;
+  if (n == 0) return SSHDP_OK;
+  return hip_status(launch_rs_reduce(inputs, n_inputs, in_dtype == SSHDP_RS_BF16, out,
+                                     out_mode == SSHDP_RS_OUT_BF16_SR, n, seed, ctr, g0,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int sshdp_rs_accumulate(const void *const *inputs, int32_t n_inputs, int32_t in_dtype, float *g, int64_t n,
+                        int32_t first, void *stream) {
+  int st = rs_check(inputs, n_inputs, in_dtype, g, n, 0);
+  if (st != SSHDP_OK) return st;
+  if (n == 0) return SSHDP_OK;
+  return hip_status(launch_rs_accumulate(inputs, n_inputs, in_dtype == SSHDP_RS_BF16, g, n, first != 0,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int sshdp_update_step(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_muon_hp *mh,
                       const sshdp_adamw_hp *ah, int64_t step, void *ws, size_t ws_bytes, void *stream) {
   int st = check_plan(p);

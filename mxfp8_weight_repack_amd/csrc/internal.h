@@ -17,6 +17,7 @@ constexpr int kNsLarge = 256;        // ... or 256 x 256 (8 waves), chosen per g
 constexpr int kMaxLanes = 4;         // Newton-Schulz groups run on up to 4 concurrent streams
 constexpr int kChunk = 4096;         // elements per AdamW / requant work item
 constexpr size_t kAlign = 256;       // workspace sub-buffer alignment (bytes)
+constexpr int kRsMaxInputs = 8;      // slices one reduce-scatter reduction call takes
 
 // One Muon unit as the kernels see it (device table, ordered by group).
 struct MuonUnit {
@@ -168,4 +169,8 @@ hipError_t launch_quant(const sshdp_plan &p, int64_t first, int64_t count, bool 
                         const sshdp_adamw_hp *hp, int64_t step, hipStream_t s);
 hipError_t launch_quant32(const sshdp_plan &p, const float *w, uint8_t *codes, uint8_t *scales, hipStream_t s);
 hipError_t launch_cast_bf16(const sshdp_plan &p, const float *w, uint16_t *out, hipStream_t s);
+hipError_t launch_rs_reduce(const void *const *inputs, int n_in, int in_bf16, void *out, int out_sr, int64_t n,
+                            uint64_t seed, uint64_t ctr, int64_t g0, hipStream_t s);
+hipError_t launch_rs_accumulate(const void *const *inputs, int n_in, int in_bf16, float *g, int64_t n, int first,
+                                hipStream_t s);
 }  // namespace sshdp
