@@ -1,6 +1,7 @@
 """Benchmark: one MI355X's share of the SS-HSDP update phase.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--config 2] [--layout L] [--no-cpu]
+    python bench.py --part rs [--config N]      (the reduce-scatter tail)
 
 A step is one sshdp_update_step over the whole workload: Muon momentum,
 batched bf16 MFMA Newton-Schulz, main-weight update, AdamW, and the MXFP8
@@ -10,11 +11,16 @@ transformer block (d=2048, 16 heads of 128, 4 KV heads, MLP 8192, per-head
 QKV Muon units), the configuration the metric is quoted on.
 
 Prints one JSON line.  `value` = parameters updated per second (padding
-excluded) from hipEvents around K steps on the launch stream.  `roofline`
-describes the dominant kernel (the Newton-Schulz MFMA contraction): its
-algorithmic flops per launch divided by its average launch duration, from
-HIP events bracketing every launch in a second pass of K steps.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+excluded) from HIP events around K steps on the launch stream (`step_ms`:
+median/min/max of the single steps).  `roofline` covers the Newton-Schulz
+phase, the dominant part: executed MFMA flops of its tile schedule per step
+divided by the phase's time (HIP events from the fork on the launch stream to
+the join of the concurrent streams, in a second pass of K steps), against the
+dense bf16 peak; `traffic` is the phase's HBM-side bytes per step from the
+counter runs recorded in profiles/traffic.json (null when the kernel sources
+changed since).  `repack_roofline` is G (with AdamW where fused) against HBM
+bandwidth.  `cpu_baseline` times the CPU oracle on a bounded sample of the
+same workload.
 """
 
 import argparse
