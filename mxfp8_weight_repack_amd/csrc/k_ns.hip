@@ -184,6 +184,70 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
   constexpr int NR = MBM + MBN;
 
   const int nk = (int)(K / BK);
+  // CAPD: while stage `sa` (K step kt) is resident, add dscale * D from it
+  auto capd = [&](const char *sa, int kt) __attribute__((always_inline)) {
+    const int mb = kt * BK - dk0;                    // tile row held at K offset 0 of this stage
+#pragma unroll
+    for (int i = 0; i < MBM; ++i) {
+      const int bm = wm * C::WTM + i * 32;           // wave-uniform
+      if (CAPD && bm >= mb && bm < mb + BK) {
+#pragma unroll
+        for (int j = 0; j < MBN; ++j) {
+          const int n = wn * C::WTN + j * 32 + lrow;
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int kl = bm - mb + g4 * 8 + (lane >> 5) * 4;
+            const uint2 d = *reinterpret_cast<const uint2 *>(sa + C::SEGA + n * RB +
+                                                             (((kl >> 3) ^ swz<BK>(lrow)) << 4) + (kl & 7) * 2);
+            acc[i][j][g4 * 4 + 0] = fmaf(dscale, __uint_as_float(d.x << 16), acc[i][j][g4 * 4 + 0]);
+            acc[i][j][g4 * 4 + 1] = fmaf(dscale, __uint_as_float(d.x & 0xFFFF0000u), acc[i][j][g4 * 4 + 1]);
+            acc[i][j][g4 * 4 + 2] = fmaf(dscale, __uint_as_float(d.y << 16), acc[i][j][g4 * 4 + 2]);
+            acc[i][j][g4 * 4 + 3] = fmaf(dscale, __uint_as_float(d.y & 0xFFFF0000u), acc[i][j][g4 * 4 + 3]);
+          }
+        }
+      }
+    }
+  };
+
+  if (C::KS == 4 && NST == 2) {
+    // Two stages, each reloaded as soon as the barrier that ends its step has
+    // passed: the loads for step kt + 2 go out with the last slice of step kt,
+    // so they have a whole step to land.
+    dma_p(0, 0);
+    dma_q(0, 0);
+    dma_p(1, (nk > 1 ? 1 : 0) * BK);
+    dma_q(1, (nk > 1 ? 1 : 0) * BK);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::NV) : "memory");   // stage 0 landed
+    __syncthreads();
+    ldfrag(smem, 0, fa0, fb0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const char *sa = smem + (kt & 1) * C::STAGE;
+      ldfrag(sa, 1, fa1, fb1);
+      mma(fa0, fb0, NR, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      ldfrag(sa, 2, fa0, fb0);
+      mma(fa1, fb1, NR, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      ldfrag(sa, 3, fa1, fb1);
+      mma(fa0, fb0, NR, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      capd(sa, kt);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");               // stage kt + 1 landed
+      __syncthreads();                                                // stage kt consumed by all waves
+      // near the end the reload repeats the last K slice into a stage nobody
+      // reads again, so the body has no branch
+      const int kn = (kt + 2 < nk ? kt + 2 : nk - 1) * BK;
+      dma_p(kt & 1, kn);
+      dma_q(kt & 1, kn);
+      ldfrag(smem + ((kt + 1) & 1) * C::STAGE, 0, fa0, fb0);        // after the last step: unused
+      mma(fa1, fb1, NR, C::NV);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                 // trailing reloads land before
+    __syncthreads();                                                  // the caller reuses the LDS
+    return;
+  }
+
 #pragma unroll
   for (int s0 = 0; s0 < NST - 1; ++s0) {
     const int k0 = (s0 < nk ? s0 : nk - 1) * BK;
@@ -219,31 +283,7 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
       mma(fa0, fb0, NR, C::NV);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (CAPD) {
-      const int mb = kt * BK - dk0;                  // tile row held at K offset 0 of this stage
-      if (mb >= 0 && mb < C::TM) {
-#pragma unroll
-        for (int i = 0; i < MBM; ++i) {
-          const int bm = wm * C::WTM + i * 32;       // wave-uniform
-          if (bm >= mb && bm < mb + BK) {
-#pragma unroll
-            for (int j = 0; j < MBN; ++j) {
-              const int n = wn * C::WTN + j * 32 + lrow;
-#pragma unroll
-              for (int g4 = 0; g4 < 4; ++g4) {
-                const int kl = bm - mb + g4 * 8 + (lane >> 5) * 4;
-                const uint2 d = *reinterpret_cast<const uint2 *>(sa + C::SEGA + n * RB +
-                                                                 (((kl >> 3) ^ swz<BK>(lrow)) << 4) + (kl & 7) * 2);
-                acc[i][j][g4 * 4 + 0] = fmaf(dscale, __uint_as_float(d.x << 16), acc[i][j][g4 * 4 + 0]);
-                acc[i][j][g4 * 4 + 1] = fmaf(dscale, __uint_as_float(d.x & 0xFFFF0000u), acc[i][j][g4 * 4 + 1]);
-                acc[i][j][g4 * 4 + 2] = fmaf(dscale, __uint_as_float(d.y << 16), acc[i][j][g4 * 4 + 2]);
-                acc[i][j][g4 * 4 + 3] = fmaf(dscale, __uint_as_float(d.y & 0xFFFF0000u), acc[i][j][g4 * 4 + 3]);
-              }
-            }
-          }
-        }
-      }
-    }
+    capd(sa, kt);
     wait_next();
     __syncthreads();
     ldfrag(smem + ((kt + 1) % NST) * C::STAGE, 0, fa0, fb0);   // after the last step: unused
