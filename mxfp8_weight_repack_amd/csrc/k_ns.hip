@@ -26,20 +26,22 @@
 // its transpose (same map: X (X^T X) = (X X^T) X); its own layout plays the
 // role of X^T.
 //
-// One launch per stage covers every group and unit (a tile table built by the
-// planner, longest-K tiles first), so small per-head units and large matrices
-// share the machine instead of running one underfilled launch each.
+// Per stage, one launch per tile size covers every group and unit on a stream
+// (tile tables built by the planner, longest K first, in XCD-aware order);
+// groups are dealt to up to four concurrent streams, so small per-head units
+// run beside the large matrices instead of serialising latency-bound launches.
 //
-// Tile kernel: TILE x TILE per workgroup of 4 waves (2 x 2), each wave
-// (TILE/2)^2 as (TILE/64)^2 blocks of v_mfma_f32_32x32x16_bf16; K in steps of
-// 64; operands move global -> LDS with global_load_lds_dwordx4 (no VGPR
-// staging), double-buffered; 128-byte LDS rows whose 16-byte chunks are XOR-
-// swizzled so fragment reads are bank-conflict free; fragment reads for the
-// next 16-wide K slice are interleaved with the current slice's MFMAs.
+// Tile kernel: 256 x 256 per workgroup of 8 waves (2 x 4, each 128 x 64) or
+// 128 x 128 per workgroup of 4 waves (2 x 2), as 32 x 32 blocks of
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulators; K in steps of 64 through
+// two LDS stages filled by buffer loads straight into LDS (no VGPR staging),
+// each stage reloaded as soon as the barrier ending its step has passed;
+// 128-byte LDS rows whose 16-byte chunks are XOR-swizzled so fragment reads
+// are bank-conflict free; fragment reads and buffer loads are interleaved one
+// per MFMA.  Epilogue through LDS (bf16 pack in hardware), nontemporal stores.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
-#include "mx_codec.h"
 #include "lds_swizzle.h"
 #include "tile_map.h"
 
@@ -53,7 +55,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // Buffer resource word 3 for raw (untyped) gfx9-family buffer loads.
 constexpr int kBufWord3 = 0x00020000;
 
-__device__ __forceinline__ float bf16_to_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
