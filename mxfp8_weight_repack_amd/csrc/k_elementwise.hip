@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256) void k_quant32(const Q32Tile *__restrict__ til
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     wv[p] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (act) wv[p] = *reinterpret_cast<const float4 *>(w + q.base + (int64_t)(rg + 8 * p) * q.cols + 4 * c4);
+    if (act) wv[p] = load_nt(w + q.base + (int64_t)(rg + 8 * p) * q.cols + 4 * c4);
   }
 #pragma unroll
   for (int p = 0; p < 4; ++p)
@@ -389,8 +389,8 @@ __global__ __launch_bounds__(256) void k_cast_bf16(const CChunk *__restrict__ ch
     const int off = p * 2048 + 8 * t;
     live[p] = off < q.n;
     if (live[p]) {
-      a[p] = *reinterpret_cast<const float4 *>(w + q.base + off);
-      b[p] = *reinterpret_cast<const float4 *>(w + q.base + off + 4);
+      a[p] = load_nt(w + q.base + off);
+      b[p] = load_nt(w + q.base + off + 4);
     }
   }
 #pragma unroll
