@@ -8,6 +8,9 @@ compute one unit at a time.
 * MoE 64 experts: zero-gradient experts bit-identical, sampled non-zero
   experts (both orientations) against the oracle; G bit-exact on sampled
   expert regions.
+* flat ragged shard of 5e8 elements (fused AdamW + G): sampled tensors'
+  w, m, v against the oracle over two steps, their codes and scales
+  bit-exact, every padding run untouched.
 * dense block d=8192: sampled heads against the oracle; the 8192 x 8192 and
   8192 x 28672 units, too large for the fp64 oracle in a test, against the
   same quintic iteration run by torch in fp32 on the GPU (a library-routine
@@ -166,3 +169,43 @@ def test_dense_block_d8192_full_size():
     for r in q:
         sub = dict(r, rows=32)
         _check_requant_region_tile(st, r, sub)
+
+
+def test_flat_shard_5e8_full_size():
+    wl = workloads.config(4)
+    say(f"full size: {wl.name}")
+    w0, g = wl.arrays()
+    st = DeviceState(wl)
+    st.step(1)
+    st.step(2)
+    torch.cuda.synchronize()
+    res = resolve_views(wl.nodes, wl.root_numel, wl.scale_layout)
+    units = [i for i, r in enumerate(res) if r["is_unit"]]
+    rng = np.random.default_rng(4)
+    pick = sorted(set(rng.choice(units, 12, replace=False).tolist() + [units[0], units[-1]]))
+    for i in pick:
+        r = res[i]
+        a, n = r["abs"], r["rows"] * r["cols"]
+        if n > 4_000_000:                                   # a large tensor: check a window of it
+            a, n = a + (n // 2) // 32 * 32, 1 << 20
+        sl = slice(a, a + n)
+        z = np.zeros(n, np.float32)
+        w1, m1, v1 = oracle.adamw_step(w0[sl], g[sl], z, z, 1, **ADAM)
+        w2, m2, v2 = oracle.adamw_step(w1, g[sl], m1, v1, 2, **ADAM)
+        tw = st.w[a:a + n].cpu().numpy()
+        tm = st.m[a:a + n].cpu().numpy()
+        tv = st.v[a:a + n].cpu().numpy()
+        assert np.max(np.abs(tw - w2)) <= 1e-6 * np.max(np.abs(w2)), i
+        assert np.max(np.abs(tm - m2)) <= 1e-6 * np.max(np.abs(m2)), i
+        assert np.max(np.abs(tv - v2)) <= 1e-5 * np.max(np.abs(v2)), i
+        # G on the GPU-updated weight, bit-exact (1x32 blocks along the flat region)
+        # (a 1-D tensor's last block runs into its zero padding, which G quantises with it)
+        from oracle.mxfp8 import quantize_blocks_fast
+        nq = (n + 31) // 32 * 32
+        tq = st.w[a:a + nq].cpu().numpy()
+        c_ref, s_ref = quantize_blocks_fast(tq.reshape(-1, 32))
+        assert np.array_equal(st.codes[a:a + nq].cpu().numpy(), c_ref.ravel()), i
+        assert np.array_equal(st.scales[a // 32:(a + nq) // 32].cpu().numpy(), s_ref.ravel()), i
+        say(f"  tensor {i} ({r['rows']}x{r['cols']}): ok")
+    for s0, n in wl.padding:
+        assert not torch.any(st.w[s0:s0 + n]).item() and not torch.any(st.m[s0:s0 + n]).item()
