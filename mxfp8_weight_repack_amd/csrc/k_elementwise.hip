@@ -20,6 +20,7 @@
 
 #include "internal.h"
 #include "mx_codec.h"
+#include "mx_device.h"
 
 namespace sshdp {
 namespace {
@@ -196,38 +197,16 @@ __global__ __launch_bounds__(256) void k_adamw(const ASeg *__restrict__ segs, fl
 }
 
 // ----------------------------------------------------------------------------- G (+ AdamW)
-// One chunk (<= kChunk elements, whole 32-blocks) per workgroup; four passes of
-// 1024 elements, each lane owning 4 consecutive elements, 8 lanes per block.
-// All loads of a chunk are issued before any arithmetic.
 // Quantise 4 elements per lane (8 lanes = one 32-element block) and store
 // their codes and the block's scale byte.  All 64 lanes must call it (the
 // block amax is a butterfly over lane groups of 8); `live` masks the stores.
 __device__ __forceinline__ void quant_store(const float4 &wv, int64_t e, bool live, int t, const QChunk &q,
                                             const QRegion *__restrict__ regions, int tile_layout,
                                             uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
-  // block amax over 8 lanes (an integer max of |x| bits also ranks NaN > Inf)
-  const uint32_t b0 = fbits(wv.x), b1 = fbits(wv.y), b2 = fbits(wv.z), b3 = fbits(wv.w);
-  uint32_t a = max(max(b0 & 0x7FFFFFFFu, b1 & 0x7FFFFFFFu), max(b2 & 0x7FFFFFFFu, b3 & 0x7FFFFFFFu));
-  a = max(a, (uint32_t)__shfl_xor((int)a, 1));
-  a = max(a, (uint32_t)__shfl_xor((int)a, 2));
-  a = max(a, (uint32_t)__shfl_xor((int)a, 4));
+  const uint32_t a = mx_amax8(wv);
   if (!live) return;
   const uint32_t sb = mx_scale_byte(a);
-  uint32_t packed;
-  if (sb == 0xFFu) {
-    packed = 0x7F7F7F7Fu;
-  } else {
-    // y = x * 2^-e is exact down to 2^-126 (and anything smaller encodes as a
-    // signed zero either way); gfx950's packed fp8 convert is OCP E4M3FN with
-    // round-to-nearest-even, bit-identical to mx_e4m3_code for every finite
-    // |y| <= 448 (checked exhaustively on the device)
-    const int ex = 127 - (int)sb;
-    const float y0 = ldexpf(wv.x, ex), y1 = ldexpf(wv.y, ex), y2 = ldexpf(wv.z, ex), y3 = ldexpf(wv.w, ex);
-    int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-    pk = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, pk, true);
-    packed = (uint32_t)pk;
-  }
-  __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t *>(codes + e));
+  __builtin_nontemporal_store(mx_encode4(wv, sb), reinterpret_cast<uint32_t *>(codes + e));
   if ((t & 7) == 0) {
     int64_t idx = e >> 5;
     if (tile_layout) {
@@ -236,10 +215,7 @@ __device__ __forceinline__ void quant_store(const float4 &wv, int64_t e, bool li
       const QRegion r = regions[q.region];
       const uint32_t col = (uint32_t)q.col0 + (uint32_t)(e - q.base);
       const uint32_t dn = col / (uint32_t)r.cols;
-      const int64_t n = (int64_t)q.row0 + dn;
-      const uint32_t kb = (col - dn * (uint32_t)r.cols) >> 5;
-      const int64_t KB = r.cols >> 5;
-      idx = (r.abs >> 5) + ((n >> 5) * (KB >> 2) + (kb >> 2)) * 128 + (n & 31) * 4 + (kb & 3);
+      idx = mx_tile32x4_index(r.abs, r.cols >> 5, (int64_t)q.row0 + dn, (col - dn * (uint32_t)r.cols) >> 5);
     }
     scales[idx] = (uint8_t)sb;
   }
@@ -360,18 +336,10 @@ __global__ __launch_bounds__(256) void k_quant32(const Q32Tile *__restrict__ til
   a = max(max(red[0][blk], red[1][blk]), max(red[2][blk], red[3][blk]));
   if (!act) return;
   const uint32_t sb = mx_scale_byte(a);
-  const int ex = 127 - (int)sb;
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    uint32_t packed = 0x7F7F7F7Fu;
-    if (sb != 0xFFu) {
-      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(wv[p].x, ex), ldexpf(wv[p].y, ex), 0, false);
-      pk = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(wv[p].z, ex), ldexpf(wv[p].w, ex), pk, true);
-      packed = (uint32_t)pk;
-    }
-    __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t *>(codes + q.base + (int64_t)(rg + 8 * p) * q.cols +
-                                                                     4 * c4));
-  }
+  for (int p = 0; p < 4; ++p)
+    __builtin_nontemporal_store(mx_encode4(wv[p], sb),
+                                reinterpret_cast<uint32_t *>(codes + q.base + (int64_t)(rg + 8 * p) * q.cols + 4 * c4));
   if (rg == 0 && (c4 & 7) == 0) scales[q.sidx + blk] = (uint8_t)sb;
 }
 

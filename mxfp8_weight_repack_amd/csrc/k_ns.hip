@@ -94,6 +94,16 @@ struct Cfg {
 template <int BK>
 __device__ __forceinline__ int swz(int r) { return lds_swz<BK>(r); }
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// the main weight is read and written once per step: keep it out of the caches
+__device__ __forceinline__ float4 load_nt4(const float *p) {
+  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_nt4(float *p, const float4 &v) {
+  __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4_t *>(p));
+}
+
 // acc = P[TM x K] Q[TN x K]^T, P and Q row-major with row pitch K elements
 // (bf16) starting at byte addresses gP, gQ (uniform).
 //
@@ -429,12 +439,12 @@ __device__ __forceinline__ void final_tile(const f32x16_t (&acc)[C::MBM][C::MBN]
         if (row < r_unit && col < c_unit) {
           float4 *pw = reinterpret_cast<float4 *>(w + u.abs + (int64_t)row * u.row_stride + col);
           const float4 xv = *reinterpret_cast<const float4 *>(&lt[li * PW + j4]);
-          float4 wv = *pw;
+          float4 wv = load_nt4(reinterpret_cast<const float *>(pw));
           wv.x = fmaf(wv.x, decay, -ls * xv.x);
           wv.y = fmaf(wv.y, decay, -ls * xv.y);
           wv.z = fmaf(wv.z, decay, -ls * xv.z);
           wv.w = fmaf(wv.w, decay, -ls * xv.w);
-          *pw = wv;
+          store_nt4(reinterpret_cast<float *>(pw), wv);
         }
       }
     } else {
@@ -446,12 +456,12 @@ __device__ __forceinline__ void final_tile(const f32x16_t (&acc)[C::MBM][C::MBN]
         if (row < r_unit && col < c_unit) {
           float4 *pw = reinterpret_cast<float4 *>(w + u.abs + (int64_t)col * u.row_stride + row);
           const float4 xv = *reinterpret_cast<const float4 *>(&lt[lc * PT + i4]);
-          float4 wv = *pw;
+          float4 wv = load_nt4(reinterpret_cast<const float *>(pw));
           wv.x = fmaf(wv.x, decay, -ls * xv.x);
           wv.y = fmaf(wv.y, decay, -ls * xv.y);
           wv.z = fmaf(wv.z, decay, -ls * xv.z);
           wv.w = fmaf(wv.w, decay, -ls * xv.w);
-          *pw = wv;
+          store_nt4(reinterpret_cast<float *>(pw), wv);
         }
       }
     }
