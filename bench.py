@@ -127,6 +127,21 @@ def cpu_baseline(wl, budget_s):
             "seconds": dt}
 
 
+def run_env(torch, wl):
+    """What the numbers were taken on: device, software versions, host cores
+    and the input seeds."""
+    p = torch.cuda.get_device_properties(0)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count()
+    return {"device": p.name, "gcn_arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "l2_bytes": getattr(p, "L2_cache_size", None), "hbm_gib": round(p.total_memory / 2 ** 30, 1),
+            "torch": torch.__version__, "hip": torch.version.hip,
+            "host_cores": cores,
+            "seeds": f"numpy PCG64(SeedSequence([{wl.config_id}, stream])), stream 0 = w, 1 = g, 2 = structure"}
+
+
 def bench_rs(args, wl):
     """The reduce-scatter tail at the workload's gradient size: a local
     reducer sums 4 BF16 slices into a BF16 partial with stochastic rounding
@@ -291,6 +306,7 @@ def main():
                    "scale_layout": layout, "ns_tflop_per_step": st["ns_flops"] / 1e12},
         "roofline": roofline, "repack_roofline": repack, "components": components,
     }
+    out["env"] = run_env(torch, wl)
     if not args.no_cpu:
         cb = cpu_baseline(wl, args.cpu_budget)
         cb.pop("seconds", None)
