@@ -174,9 +174,12 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
     g.n = (int32_t)kv.second.size();
     {
       // 256 x 256 tiles where the group is large enough to fill the machine with them
-      // (and padding to 256 costs little); 128 x 128 otherwise
+      // and padding to 256 adds at most ~6% flops (r²c) over padding to 128; 128 x 128
+      // otherwise (r = 1408 pads to 1536, +19%: measured slower than 128 tiles)
       const int64_t t256 = (g.r + kNsLarge - 1) / kNsLarge, c256 = (g.c + kNsLarge - 1) / kNsLarge;
-      const bool big = g.r >= 1024;
+      const double r2 = (double)round_up(g.r, kNsLarge) / round_up(g.r, kNsSmall);
+      const double c2 = (double)round_up(g.c, kNsLarge) / round_up(g.c, kNsSmall);
+      const bool big = g.r >= 1024 && r2 * r2 * c2 <= 1.06;
       g.tile_u = big && t256 * c256 * g.n >= 128 ? kNsLarge : kNsSmall;
       g.tile_g = big && t256 * (t256 + 1) / 2 * g.n >= 192 ? kNsLarge : kNsSmall;
       g.r_pad = (int32_t)round_up(g.r, std::max(g.tile_g, g.tile_u));
