@@ -68,6 +68,17 @@ __global__ __launch_bounds__(256) void k_f0(const MuonUnit *__restrict__ units, 
   const int col = tl.tc * T + cq * 4;
   uint16_t *orig = reinterpret_cast<uint16_t *>(ws + u.ws_orig);
   uint16_t *trans = reinterpret_cast<uint16_t *>(ws + u.ws_trans);
+  // all eight 16-byte loads first, so each lane has them in flight together
+  float4 gvs[4], mvs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = tl.tr * T + r0 + 16 * i;
+    if (row < u.rows && col < u.cols) {
+      const int64_t e = u.abs + (int64_t)row * u.row_stride + col;
+      gvs[i] = load_nt(g + e);
+      mvs[i] = load_nt(m + e);
+    }
+  }
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -76,8 +87,8 @@ __global__ __launch_bounds__(256) void k_f0(const MuonUnit *__restrict__ units, 
     uint32_t b[4] = {0u, 0u, 0u, 0u};
     if (row < u.rows && col < u.cols) {
       const int64_t e = u.abs + (int64_t)row * u.row_stride + col;
-      const float4 gv = load_nt(g + e);
-      float4 mv = load_nt(m + e);
+      const float4 gv = gvs[i];
+      float4 mv = mvs[i];
       mv.x = fmaf(mu, mv.x, gv.x);
       mv.y = fmaf(mu, mv.y, gv.y);
       mv.z = fmaf(mu, mv.z, gv.z);
