@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--layout", choices=["rowmajor", "tile32x4", "block32x32"], default=None,
                     help="scale layout (default: the workload's own); block32x32 = one scale per 32x32 block")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--cpu-budget", type=float, default=25.0, help="seconds of oracle work to aim for")
     ap.add_argument("--part", choices=["step", "rs"], default="step",
                     help="step: the update step (default); rs: the reduce-scatter tail on the workload's "
@@ -255,6 +256,28 @@ def main():
     per_step = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps))
     value = wl.params / (ms / 1e3)
 
+    # the same step captured once into a HIP graph (side streams joined inside the
+    # capture) and replayed K times: the launch sequence without the host in the loop
+    graph_ms = None
+    if not args.no_graph:
+        gstream = torch.cuda.Stream()
+        gstream.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gstream):
+            sh.update_step(plan, bufs, mhp, ahp, step + 1, ws, ws_bytes, gstream.cuda_stream)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        gev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        gev[0].record()
+        for _ in range(args.steps):
+            graph.replay()
+        gev[1].record()
+        torch.cuda.synchronize()
+        graph_ms = gev[0].elapsed_time(gev[1]) / args.steps
+        step += 1 + args.warmup + args.steps
+        del graph
+
     # per-kernel-class durations: HIP events bracketing every launch, same K steps
     plan.profile(True)
     for _ in range(args.steps):
@@ -305,6 +328,7 @@ def main():
                    "ns_groups": [[gi["r"], gi["c"], gi["n_units"]] for gi in plan.groups()],
                    "scale_layout": layout, "ns_tflop_per_step": st["ns_flops"] / 1e12},
         "roofline": roofline, "repack_roofline": repack, "components": components,
+        "graph_ms_per_step": graph_ms,
     }
     out["env"] = run_env(torch, wl)
     if not args.no_cpu:

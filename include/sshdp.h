@@ -24,8 +24,9 @@
  * offsets; views are described by a data tree [SS-HSDP §3.2 "Data Tree"]: a
  * child is a view at an element offset inside its parent, only the root owns
  * storage.  Codes mirror the fp32 root byte-for-element, so a head's codes are a
- * sub-range of its packed projection's codes.  Scales are one byte per 32
- * elements, in one of two layouts (see SSHDP_SCALE_*).
+ * sub-range of its packed projection's codes.  Scales are one E8M0 byte per
+ * 1x32 block (row-major or the 32x128 tile layout) or per 32x32 block (see
+ * SSHDP_SCALE_*).
  *
  * Conventions.  All functions return an int status: SSHDP_OK (0) or a negative
  * SSHDP_ERR_* code; sshdp_status_string() names it.  Device pointers are
@@ -207,7 +208,9 @@ int sshdp_default_opts(sshdp_plan_opts *opts);
  * groups; Appendix A Table 4 rejections].  Host-synchronous; unless
  * SSHDP_PLAN_HOST_ONLY, allocates and uploads one block of device descriptor
  * tables on the current HIP device.  Errors leave *out_plan NULL and touch no
- * device memory.  The plan is freed by sshdp_plan_destroy. */
+ * device memory.  The plan is freed by sshdp_plan_destroy, which releases its
+ * device tables and side streams: call it only once the work enqueued with the
+ * plan has completed. */
 int sshdp_plan_views(const sshdp_node *nodes, int32_t n_nodes, int64_t root_numel,
                      const sshdp_plan_opts *opts, sshdp_plan **out_plan);
 

@@ -298,6 +298,35 @@ def test_determinism_and_resume():
         assert np.array_equal(ha[k].view(np.uint8), hd[k].view(np.uint8)), k
 
 
+def test_update_step_captured_in_a_hip_graph():
+    """The whole step (side streams forked and joined by events) captured into
+    a HIP graph and replayed three times, with eager work and synchronisation
+    between replays: after every replay the state equals the same number of
+    eager calls bit for bit.  The step counter is baked into the capture, so
+    both sides repeat step 1."""
+    for wl in (workloads.config(2, small=True), workloads.ragged_mix()):
+        say(f"graph capture {wl.name}")
+        eager = DeviceState(wl)
+        cap = DeviceState(wl)
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(graph, stream=side):
+            sh.update_step(cap.plan, cap.bufs(), sh.muon_hp(**MUON), sh.adamw_hp(**ADAM), 1, cap.ws, cap.ws_bytes,
+                           side.cuda_stream)
+        torch.cuda.synchronize()
+        assert torch.equal(cap.w, eager.w)            # capturing ran nothing
+        for k in range(3):
+            graph.replay()
+            eager.step(1)
+            torch.cuda.synchronize()
+            hc, he = cap.host(), eager.host()
+            for key in he:
+                assert np.array_equal(hc[key].view(np.uint8), he[key].view(np.uint8)), (wl.name, k, key)
+            eager.g.mul_(1.0)                         # unrelated eager work between replays
+        del graph
+
+
 def test_multi_step_against_oracle():
     """Three steps: momentum and AdamW state evolve on both sides."""
     wl = workloads.config(1)
