@@ -1,6 +1,6 @@
 """Benchmark: one MI355X's share of the SS-HSDP update phase.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--layout L] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--config 2] [--layout L] [--no-cpu] [--no-graph]
     python bench.py --part rs [--config N]      (the reduce-scatter tail)
 
 A step is one sshdp_update_step over the whole workload: Muon momentum,
@@ -19,8 +19,9 @@ the join of the concurrent streams, in a second pass of K steps), against the
 dense bf16 peak; `traffic` is the phase's HBM-side bytes per step from the
 counter runs recorded in profiles/traffic.json (null when the kernel sources
 changed since).  `repack_roofline` is G (with AdamW where fused) against HBM
-bandwidth.  `cpu_baseline` times the CPU oracle on a bounded sample of the
-same workload.
+bandwidth.  `graph_ms_per_step` is the same step captured once into a HIP
+graph and replayed K times (context only; `value` is the eager figure).
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
 
 import argparse
