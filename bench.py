@@ -93,9 +93,12 @@ def cpu_baseline(wl, budget_s):
     from oracle.views import resolve_views, unit_indices
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in blas] or [1])
+        backend = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version', '')}".strip() for i in blas}))
     except Exception:  # pragma: no cover
-        threads = 1
+        threads, backend = 1, "unknown BLAS"
+    backend = backend or "unknown BLAS"
     w0, g = wl.arrays()
     res = resolve_views(wl.nodes, wl.root_numel, wl.scale_layout)
     # cost model for picking the sample: ~0.3 us/element elementwise, ~25 GF/s per BLAS thread for NS
@@ -125,7 +128,7 @@ def cpu_baseline(wl, budget_s):
     dt = time.perf_counter() - t0
     return {"value": params / dt, "unit": "params/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(sub)} of {len(wl.units())} units ({params} params, one full update step "
-                      f"incl. their MXFP8 repack) in {dt:.1f} s; NumPy/OpenBLAS fp64, {threads} BLAS threads",
+                      f"incl. their MXFP8 repack) in {dt:.1f} s; NumPy fp64 on {backend}, {threads} BLAS threads",
             "seconds": dt}
 
 
@@ -137,10 +140,16 @@ def run_env(torch, wl):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         cores = os.cpu_count()
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:  # pragma: no cover
+        pass
     return {"device": p.name, "gcn_arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
             "l2_bytes": getattr(p, "L2_cache_size", None), "hbm_gib": round(p.total_memory / 2 ** 30, 1),
             "torch": torch.__version__, "hip": torch.version.hip,
-            "host_cores": cores,
+            "host_cores": cores, "host_cpu": cpu,
             "seeds": f"numpy PCG64(SeedSequence([{wl.config_id}, stream])), stream 0 = w, 1 = g, 2 = structure"}
 
 
