@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SSHDP_ABI_VERSION 2
+#define SSHDP_ABI_VERSION 3
 
 /* Status codes.  The planning errors are the rejections of [SS-HSDP Appendix A,
  * Table 4]: incompatible metadata, invalid geometry, storage overlap. */
@@ -91,9 +91,15 @@ enum { SSHDP_OPT_NONE = 0, SSHDP_OPT_MUON = 1, SSHDP_OPT_ADAMW = 2 };
  * fused with G (the AdamW units run first, then G). */
 enum { SSHDP_SCALE_ROWMAJOR = 0, SSHDP_SCALE_TILE32X4 = 1, SSHDP_SCALE_BLOCK32X32 = 2 };
 
-/* Plan flags. */
+/* Plan flags.  The Newton-Schulz tile policy is a tuning knob (results stay
+ * within the Newton-Schulz tolerance either way, not bit-identical): by default
+ * a group's products run in 256 x 256 tiles over their largest 256-aligned
+ * leading block when the group is large enough to fill the GPU with them, and
+ * in 128 x 128 tiles elsewhere.  Setting both tile flags is an argument error. */
 enum {
-  SSHDP_PLAN_HOST_ONLY = 1  /* plan and validate on the host; no device tables (cannot launch) */
+  SSHDP_PLAN_HOST_ONLY = 1,       /* plan and validate on the host; no device tables (cannot launch) */
+  SSHDP_PLAN_NS_TILES_SMALL = 2,  /* every Newton-Schulz product in 128 x 128 tiles                  */
+  SSHDP_PLAN_NS_TILES_LARGE = 4   /* 256 x 256 tiles over every 256-aligned leading block            */
 };
 
 /* One data-tree node [SS-HSDP §3.2]: a 2-D view (rows x cols, cols contiguous,
@@ -195,10 +201,15 @@ typedef struct {
  * (r = min(rows, cols)), run as one batched GEMM per stage [SS-HSDP §4.1]. */
 typedef struct {
   int32_t r, c;               /* oriented shape                                            */
-  int32_t r_pad, c_pad;       /* padded to the GEMM tile                                   */
+  int32_t r_pad, c_pad;       /* padded to a multiple of 128                               */
   int32_t n_units;
-  int32_t tile;               /* macro-tile edge of the update product (128 or 256)        */
-  int32_t tile_gram;          /* macro-tile edge of the Gram and polynomial products       */
+  int32_t tile;               /* largest macro-tile edge of the update product (128 or 256) */
+  int32_t tile_gram;          /* largest macro-tile edge of the Gram and polynomial products */
+  int32_t gram256;            /* Gram/poly rows and columns [0, gram256) run in 256-tiles,  */
+                              /* the rest in 128-tiles (0: all 128)                          */
+  int32_t upd256_rows;        /* update rows [0, upd256_rows) x columns [0, upd256_cols)    */
+  int32_t upd256_cols;        /* run in 256-tiles, the rest in 128-tiles                     */
+  int32_t pad_;
 } sshdp_group_info;
 
 /* Fill *opts with the defaults above. */

@@ -22,6 +22,8 @@ ERROR_NAMES = {ERR_ARG: "ARG", ERR_TREE: "TREE", ERR_BOUNDS: "BOUNDS", ERR_OVERL
 OPT = {None: 0, "muon": 1, "adamw": 2}
 LAYOUT = {"rowmajor": 0, "tile32x4": 1, "block32x32": 2}
 PLAN_HOST_ONLY = 1
+# Newton-Schulz tile policy: planner default, all 128 x 128, or 256 x 256 over every 256-aligned block
+NS_TILES = {"auto": 0, "small": 2, "large": 4}
 PROF_CLASSES = ["momentum", "norm", "ns_gram", "ns_poly", "ns_update", "adamw", "adamw_requant", "requant",
                 "ns_phase", "cast_bf16"]
 # node["quantize"]: False/None (no G), True or "mxfp8" (MXFP8 codes + scales), "bf16" (bfloat16 cast)
@@ -76,7 +78,8 @@ class PlanStats(ctypes.Structure):
 class GroupInfo(ctypes.Structure):
     _fields_ = [("r", ctypes.c_int32), ("c", ctypes.c_int32), ("r_pad", ctypes.c_int32),
                 ("c_pad", ctypes.c_int32), ("n_units", ctypes.c_int32), ("tile", ctypes.c_int32),
-                ("tile_gram", ctypes.c_int32)]
+                ("tile_gram", ctypes.c_int32), ("gram256", ctypes.c_int32), ("upd256_rows", ctypes.c_int32),
+                ("upd256_cols", ctypes.c_int32), ("pad_", ctypes.c_int32)]
 
 
 # every symbol include/sshdp.h declares, with its argument and return types
@@ -182,13 +185,14 @@ class Plan:
     """A resolved data tree (sshdp_plan_views) and its tables."""
 
     def __init__(self, nodes, root_numel, layout="rowmajor", ns_steps=5, ns_a=3.4445, ns_b=-4.7750, ns_c=2.0315,
-                 ns_eps=1e-7, nesterov=False, scale_mode=0, host_only=False):
+                 ns_eps=1e-7, nesterov=False, scale_mode=0, host_only=False, ns_tiles="auto"):
         o = default_opts()
         o.ns_steps, o.ns_a, o.ns_b, o.ns_c, o.ns_eps = ns_steps, ns_a, ns_b, ns_c, ns_eps
         o.scale_layout = LAYOUT[layout]
         o.nesterov = int(bool(nesterov))
         o.muon_scale_mode = scale_mode
-        o.flags = PLAN_HOST_ONLY if host_only else 0
+        # an unknown policy sets both tile flags, which the library rejects (ARG)
+        o.flags = (PLAN_HOST_ONLY if host_only else 0) | NS_TILES.get(ns_tiles, 6)
         self._nodes = node_array(nodes)
         self._h = ctypes.c_void_p()
         self.layout = layout

@@ -45,7 +45,9 @@ struct F0Tile {
 // Newton-Schulz group: units with the same oriented shape r x c (r <= c).
 struct Group {
   int32_t r, c, r_pad, c_pad, n;
-  int32_t tile_g, tile_u;   // macro tile of the Gram/poly products and of the update product
+  // 256-tile regions (multiples of 256; 0 = none); the rest of each product in 128-tiles:
+  // Gram/poly rows and columns [0, g256), update rows [0, u256r) x columns [0, u256c)
+  int32_t g256, u256r, u256c;
   int32_t unit_base;    // first MuonUnit of the group in the device table
   size_t off_x, off_xt0, off_xt1, off_a, off_b;   // workspace byte offsets
 };

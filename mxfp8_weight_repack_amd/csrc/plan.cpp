@@ -173,17 +173,24 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
     g.c = (int32_t)kv.first.second;
     g.n = (int32_t)kv.second.size();
     {
-      // 256 x 256 tiles where the group is large enough to fill the machine with them
-      // and padding to 256 adds at most ~6% flops (r²c) over padding to 128; 128 x 128
-      // otherwise (r = 1408 pads to 1536, +19%: measured slower than 128 tiles)
-      const int64_t t256 = (g.r + kNsLarge - 1) / kNsLarge, c256 = (g.c + kNsLarge - 1) / kNsLarge;
-      const double r2 = (double)round_up(g.r, kNsLarge) / round_up(g.r, kNsSmall);
-      const double c2 = (double)round_up(g.c, kNsLarge) / round_up(g.c, kNsSmall);
-      const bool big = g.r >= 1024 && r2 * r2 * c2 <= 1.06;
-      g.tile_u = big && t256 * c256 * g.n >= 128 ? kNsLarge : kNsSmall;
-      g.tile_g = big && t256 * (t256 + 1) / 2 * g.n >= 192 ? kNsLarge : kNsSmall;
-      g.r_pad = (int32_t)round_up(g.r, std::max(g.tile_g, g.tile_u));
-      g.c_pad = (int32_t)round_up(g.c, g.tile_u);
+      // Padding is to 128.  The largest 256-aligned leading block of each product runs in
+      // 256 x 256 tiles where the group has enough of them to fill the machine (update: >= 128
+      // tiles; Gram/poly: >= 192 triangle tiles, and r >= 4096 so the poly's contraction is
+      // long enough to amortise a 256-tile's fill and two-sided store); the ragged strip
+      // beyond it, or the whole product otherwise, in 128 x 128 tiles.  (MoE r = 1408: the
+      // update in 256-tiles over 1280 rows plus a 128 strip, the Gram/poly in 128-tiles;
+      // padding to 1536 instead costs 19% more flops.)
+      g.r_pad = (int32_t)round_up(g.r, kNsSmall);
+      g.c_pad = (int32_t)round_up(g.c, kNsSmall);
+      const int64_t R2 = g.r_pad / kNsLarge, C2 = g.c_pad / kNsLarge;   // whole 256-tiles per edge
+      const bool small = (p.opts.flags & SSHDP_PLAN_NS_TILES_SMALL) != 0;
+      const bool large = (p.opts.flags & SSHDP_PLAN_NS_TILES_LARGE) != 0;
+      const bool big = !small && (large || g.r >= 1024);
+      const bool upd = big && R2 * C2 > 0 && (large || R2 * C2 * g.n >= 128);
+      const bool gram = big && R2 > 0 && (large || (R2 * (R2 + 1) / 2 * g.n >= 192 && g.r >= 4096));
+      g.u256r = upd ? (int32_t)(R2 * kNsLarge) : 0;
+      g.u256c = upd ? (int32_t)(C2 * kNsLarge) : 0;
+      g.g256 = gram ? (int32_t)(R2 * kNsLarge) : 0;
     }
     g.n = (int32_t)kv.second.size();
     g.unit_base = (int32_t)p.munits.size();
@@ -234,13 +241,16 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
     }
   }
   p.ws_bytes = off;
-  // per-group cost (executed MFMA flops per step), groups dealt to lanes largest first
+  // per-group cost (executed MFMA flops per NS step), groups dealt to lanes largest first
   std::vector<double> cost(p.groups.size(), 0.0);
   for (size_t gi = 0; gi < p.groups.size(); ++gi) {
     const Group &g = p.groups[gi];
-    const double tg = g.tile_g, tu = g.tile_u;
-    const double ntg = g.r_pad / g.tile_g, ntr = g.r_pad / g.tile_u, ntc = g.c_pad / g.tile_u;
-    cost[gi] = g.n * (ntg * (ntg + 1) / 2 * tg * tg * 2.0 * (g.c_pad + g.r_pad) + ntr * ntc * tu * tu * 2.0 * g.r_pad);
+    const double L = kNsLarge, S = kNsSmall;
+    const double n2 = g.g256 / kNsLarge, n1 = g.r_pad / kNsSmall, s1 = g.g256 / kNsSmall;
+    const double tri = n2 * (n2 + 1) / 2 * L * L + ((n1 * (n1 + 1) - s1 * (s1 + 1)) / 2) * S * S;
+    const double u2 = (double)(g.u256r / kNsLarge) * (g.u256c / kNsLarge) * L * L;
+    const double u1 = ((double)g.r_pad * g.c_pad - (double)g.u256r * g.u256c);
+    cost[gi] = g.n * (tri * 2.0 * (g.c_pad + g.r_pad) + (u2 + u1) * 2.0 * g.r_pad);
   }
   std::vector<size_t> order(p.groups.size());
   for (size_t i = 0; i < order.size(); ++i) order[i] = i;
@@ -263,16 +273,28 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
     p.ns_groups.push_back({(int64_t)g.off_x, (int64_t)g.off_xt0, (int64_t)g.off_xt1, (int64_t)g.off_a,
                            (int64_t)g.off_b, g.r_pad, g.c_pad, g.unit_base, g.n});
     const int ln = p.group_lane[gi];
-    const int sg = g.tile_g == kNsLarge, su = g.tile_u == kNsLarge;
-    const int ntg = g.r_pad / g.tile_g, ntr = g.r_pad / g.tile_u, ntc = g.c_pad / g.tile_u;
+    const int n2 = g.g256 / kNsLarge, n1 = g.r_pad / kNsSmall, s1 = g.g256 / kNsSmall;
+    const int ur2 = g.u256r / kNsLarge, uc2 = g.u256c / kNsLarge;
+    const int ur1 = g.u256r / kNsSmall, uc1 = g.u256c / kNsSmall, nr1 = g.r_pad / kNsSmall, nc1 = g.c_pad / kNsSmall;
     for (int b = 0; b < g.n; ++b) {
-      for (int tm = 0; tm < ntg; ++tm)
-        for (int tn = tm; tn < ntg; ++tn) {
-          p.ns_tiles[ln][0][sg].push_back({(int32_t)gi, b, tm, tn});
-          p.ns_tiles[ln][1][sg].push_back({(int32_t)gi, b, tm, tn});
+      // Gram/poly (symmetric, tm <= tn, mirrored): 256-tiles on [0, g256)^2, 128-tiles on
+      // the column strip [g256, r_pad) (their mirrors fill the row strip)
+      for (int tm = 0; tm < n2; ++tm)
+        for (int tn = tm; tn < n2; ++tn) {
+          p.ns_tiles[ln][0][1].push_back({(int32_t)gi, b, tm, tn});
+          p.ns_tiles[ln][1][1].push_back({(int32_t)gi, b, tm, tn});
         }
-      for (int tm = 0; tm < ntr; ++tm)
-        for (int tn = 0; tn < ntc; ++tn) p.ns_tiles[ln][2][su].push_back({(int32_t)gi, b, tm, tn});
+      for (int tn = s1; tn < n1; ++tn)
+        for (int tm = 0; tm <= tn; ++tm) {
+          p.ns_tiles[ln][0][0].push_back({(int32_t)gi, b, tm, tn});
+          p.ns_tiles[ln][1][0].push_back({(int32_t)gi, b, tm, tn});
+        }
+      // update: 256-tiles on [0, u256r) x [0, u256c), 128-tiles on the rest
+      for (int tm = 0; tm < ur2; ++tm)
+        for (int tn = 0; tn < uc2; ++tn) p.ns_tiles[ln][2][1].push_back({(int32_t)gi, b, tm, tn});
+      for (int tm = 0; tm < nr1; ++tm)
+        for (int tn = 0; tn < nc1; ++tn)
+          if (tm >= ur1 || tn >= uc1) p.ns_tiles[ln][2][0].push_back({(int32_t)gi, b, tm, tn});
     }
   }
   for (int ln = 0; ln < p.n_lanes; ++ln)
@@ -494,7 +516,8 @@ int sshdp_plan_views(const sshdp_node *nodes, int32_t n_nodes, int64_t root_nume
   if (o.ns_steps < 1 || o.ns_steps > 64 || (o.scale_layout != SSHDP_SCALE_ROWMAJOR &&
       o.scale_layout != SSHDP_SCALE_TILE32X4 && o.scale_layout != SSHDP_SCALE_BLOCK32X32) ||
       o.muon_scale_mode < 0 || o.muon_scale_mode > 2 ||
-      !(o.ns_eps >= 0.0f) || (o.flags & ~1u))
+      !(o.ns_eps >= 0.0f) || (o.flags & ~7u) ||
+      ((o.flags & SSHDP_PLAN_NS_TILES_SMALL) && (o.flags & SSHDP_PLAN_NS_TILES_LARGE)))
     return SSHDP_ERR_ARG;
   std::vector<int64_t> abs, ext;
   int st = validate(nodes, n_nodes, root_numel, o.scale_layout, abs, ext);
@@ -533,7 +556,8 @@ int sshdp_plan_group(const sshdp_plan *p, int32_t g, sshdp_group_info *info) {
   if (!p || !info || g < 0 || g >= (int32_t)p->groups.size()) return SSHDP_ERR_ARG;
   const Group &G = p->groups[g];
   info->r = G.r; info->c = G.c; info->r_pad = G.r_pad; info->c_pad = G.c_pad;
-  info->n_units = G.n; info->tile = G.tile_u; info->tile_gram = G.tile_g;
+  info->n_units = G.n; info->tile = G.u256r ? kNsLarge : kNsSmall; info->tile_gram = G.g256 ? kNsLarge : kNsSmall;
+  info->gram256 = G.g256; info->upd256_rows = G.u256r; info->upd256_cols = G.u256c;
   return SSHDP_OK;
 }
 

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
         assert name in _lib.SIGNATURES, name
     assert set(_lib.SIGNATURES) == set(decl)
-    assert L.sshdp_abi_version() == 2
+    assert L.sshdp_abi_version() == 3
     assert L.sshdp_status_string(-5) == b"geometry or metadata the kernels cannot take"
 
 
@@ -111,10 +111,21 @@ def test_planner_groups_and_stats_on_workloads():
         flops = sum(cnt * 5 * (4 * r * r * c + 2 * r ** 3) for (r, c), cnt in shapes.items())
         assert abs(st["ns_flops"] - flops) <= 1e-9 * max(flops, 1)
         for g in p.groups():
-            t = max(g["tile"], g["tile_gram"])
-            assert g["r_pad"] % t == 0 and g["c_pad"] % g["tile"] == 0
-            assert g["r_pad"] - g["r"] < t and g["c_pad"] - g["c"] < g["tile"]
-            assert g["tile"] in (128, 256) and g["tile_gram"] in (128, 256)
+            # padding to 128 only; 256-tiles cover the largest 256-aligned leading block or nothing
+            assert g["r_pad"] % 128 == 0 and g["c_pad"] % 128 == 0
+            assert 0 <= g["r_pad"] - g["r"] < 128 and 0 <= g["c_pad"] - g["c"] < 128
+            assert g["gram256"] in (0, g["r_pad"] // 256 * 256)
+            assert (g["upd256_rows"], g["upd256_cols"]) in ((0, 0), (g["r_pad"] // 256 * 256, g["c_pad"] // 256 * 256))
+            assert g["tile"] == (256 if g["upd256_rows"] else 128)
+            assert g["tile_gram"] == (256 if g["gram256"] else 128)
+    # the MoE bank (r = 1408): update in 256-tiles over the leading 1280 rows plus a 128-tile
+    # strip, Gram/poly in 128-tiles, no padding
+    wl = workloads.config(3)
+    (g,) = _plan(wl.nodes, wl.root_numel, "tile32x4").groups()
+    assert (g["r_pad"], g["c_pad"], g["gram256"], g["upd256_rows"], g["upd256_cols"]) == (1408, 2048, 0, 1280, 2048)
+    for pol, want in (("small", (0, 0, 0)), ("large", (1280, 1280, 2048))):
+        (g,) = sh.Plan(wl.nodes, wl.root_numel, layout="tile32x4", host_only=True, ns_tiles=pol).groups()
+        assert (g["gram256"], g["upd256_rows"], g["upd256_cols"]) == want
     # the flat shard's requant is fused with AdamW everywhere; the dense block's is not
     wl = workloads.config(4, small=True)
     st = _plan(wl.nodes, wl.root_numel).stats()
@@ -141,6 +152,10 @@ def test_planner_argument_errors():
     with pytest.raises(sh.SshdpError) as e:
         sh.Plan([], 10, host_only=True)
     assert e.value.name == "ARG"
+    for bad in ("bogus", None):                      # unknown policy; both tile flags set
+        with pytest.raises(sh.SshdpError) as e:
+            sh.Plan(wl.nodes, wl.root_numel, host_only=True, ns_tiles=bad)
+        assert e.value.name == "ARG"
     p = _plan(wl.nodes, wl.root_numel, "tile32x4")
     # a host-only plan refuses to launch, before touching any pointer
     b = sh.buffers(8, 16, 32, 48, 64, 80)

@@ -200,6 +200,31 @@ def test_update_step_parity(case):
     say(f"  worst NS rel-Frobenius {worst:.3e}")
 
 
+@pytest.mark.parametrize("policy", ["small", "large", "auto"])
+def test_update_step_parity_tile_policies(policy):
+    """Newton-Schulz products split into a 256-tile leading block and 128-tile
+    strips (Gram/poly: the column strip and its mirror; update: the L-shaped
+    rest) against the oracle, with every product in 128-tiles, and with the
+    planner's own choice."""
+    wl = workloads.mixed_tiles()
+    say(f"update_step {wl.name} tiles={policy}")
+    st = DeviceState(wl, plan_kw=dict(ns_tiles=policy))
+    groups = st.plan.groups()
+    if policy == "large":
+        assert any(0 < g["gram256"] < g["r_pad"] for g in groups)
+        assert any(0 < g["upd256_rows"] < g["r_pad"] for g in groups)
+        assert any(0 < g["upd256_cols"] < g["c_pad"] for g in groups)
+    if policy == "small":
+        assert all(g["gram256"] == g["upd256_rows"] == 0 for g in groups)
+    w0, g = wl.arrays()
+    st.step(1)
+    h = st.host()
+    z = np.zeros_like(w0)
+    ref, dirs = oracle_step(wl, wl.scale_layout, w0, g, z, z, 1)
+    worst = check_step(wl, wl.scale_layout, h, ref, dirs, w0)
+    say(f"  worst NS rel-Frobenius {worst:.3e}")
+
+
 @pytest.mark.parametrize("case", ["c1", "c2s", "c3s"])
 def test_update_step_parity_block32x32(case):
     """The whole step with one scale per 32x32 block: AdamW runs unfused, then

@@ -191,6 +191,19 @@ def ragged_mix(cid=100, name="ragged mix (odd shapes, strided views)"):
     return wl
 
 
+def mixed_tiles(cid=101, name="odd multiples of 128 (256-tile blocks with 128-tile strips)"):
+    """Muon units whose padded edges are odd multiples of 128, so a plan with
+    256-tiles covers each product's 256-aligned leading block and leaves a
+    128-wide strip: wide 320 x 500 (x2), tall 700 x 384, and 130 x 260."""
+    t = _Tree()
+    t.region(320, 500, unit=True, opt="muon")
+    t.region(320, 500, unit=True, opt="muon")
+    t.region(700, 384, unit=True, opt="muon", quant=True)
+    t.region(130, 260, unit=True, opt="muon")
+    t.region(1, 96, unit=True, opt="adamw", quant=True)
+    return _finish(cid, name, t, "rowmajor")
+
+
 def _finish(cid, name, t, layout):
     params = 0
     for n in t.nodes:
