@@ -95,13 +95,16 @@ template <int BK>
 __device__ __forceinline__ int swz(int r) { return lds_swz<BK>(r); }
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-// the main weight is read and written once per step: keep it out of the caches
+typedef __attribute__((address_space(1))) f32x4_t gf32x4_t;
+// the main weight is read and written once per step: keep it out of the caches.
+// The global address space keeps these off the LDS counter (a generic access
+// would be waited for by every LDS wait in between).
 __device__ __forceinline__ float4 load_nt4(const float *p) {
-  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+  const f32x4_t v = __builtin_nontemporal_load((const gf32x4_t *)p);
   return make_float4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ void store_nt4(float *p, const float4 &v) {
-  __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4_t *>(p));
+  __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w}, (gf32x4_t *)p);
 }
 
 // acc = P[TM x K] Q[TN x K]^T, P and Q row-major with row pitch K elements
@@ -430,39 +433,44 @@ __device__ __forceinline__ void final_tile(const f32x16_t (&acc)[C::MBM][C::MBN]
     }
     __syncthreads();
     const int rb = r0 + h * HM;                      // first oriented row of this pass
-    if (!u.tall) {
-      // view row i = oriented row, contiguous along oriented columns
-      constexpr int CH = C::TN / 4;
-      for (int id = t; id < HM * CH; id += C::NT) {
-        const int li = id / CH, j4 = (id - li * CH) * 4;
-        const int row = rb + li, col = c0 + j4;
-        if (row < r_unit && col < c_unit) {
-          float4 *pw = reinterpret_cast<float4 *>(w + u.abs + (int64_t)row * u.row_stride + col);
-          const float4 xv = *reinterpret_cast<const float4 *>(&lt[li * PW + j4]);
-          float4 wv = load_nt4(reinterpret_cast<const float *>(pw));
-          wv.x = fmaf(wv.x, decay, -ls * xv.x);
-          wv.y = fmaf(wv.y, decay, -ls * xv.y);
-          wv.z = fmaf(wv.z, decay, -ls * xv.z);
-          wv.w = fmaf(wv.w, decay, -ls * xv.w);
-          store_nt4(reinterpret_cast<float *>(pw), wv);
+    // each thread owns IT float4 of w per pass; they are read in batches of KB
+    // loads before any store, so a batch's loads are in flight together
+    constexpr int IT = C::TN * HM / 4 / C::NT, KB = 4;
+    static_assert(C::TN * HM / 4 % C::NT == 0 && IT % KB == 0, "whole float4 batches per thread");
+#pragma unroll
+    for (int k0 = 0; k0 < IT; k0 += KB) {
+      float *pw[KB];
+      float4 xv[KB], wv[KB];
+#pragma unroll
+      for (int q = 0; q < KB; ++q) {
+        const int id = t + (k0 + q) * C::NT;
+        int row, col, lofs;
+        if (!u.tall) {
+          // view row = oriented row, contiguous along oriented columns
+          constexpr int CH = C::TN / 4;
+          const int li = id / CH, j4 = (id - li * CH) * 4;
+          row = rb + li; col = c0 + j4; lofs = li * PW + j4;
+          pw[q] = w + u.abs + (int64_t)row * u.row_stride + col;
+        } else {
+          // view row = oriented column, contiguous along oriented rows
+          constexpr int CH = HM / 4;
+          const int lc = id / CH, i4 = (id - lc * CH) * 4;
+          row = rb + i4; col = c0 + lc; lofs = lc * PT + i4;
+          pw[q] = w + u.abs + (int64_t)col * u.row_stride + row;
         }
+        if (!(row < r_unit && col < c_unit)) pw[q] = nullptr;
+        xv[q] = *reinterpret_cast<const float4 *>(&lt[lofs]);
+        if (pw[q]) wv[q] = load_nt4(pw[q]);
       }
-    } else {
-      // view row = oriented column, contiguous along oriented rows
-      constexpr int CH = HM / 4;
-      for (int id = t; id < C::TN * CH; id += C::NT) {
-        const int lc = id / CH, i4 = (id - lc * CH) * 4;
-        const int row = rb + i4, col = c0 + lc;
-        if (row < r_unit && col < c_unit) {
-          float4 *pw = reinterpret_cast<float4 *>(w + u.abs + (int64_t)col * u.row_stride + row);
-          const float4 xv = *reinterpret_cast<const float4 *>(&lt[lc * PT + i4]);
-          float4 wv = load_nt4(reinterpret_cast<const float *>(pw));
-          wv.x = fmaf(wv.x, decay, -ls * xv.x);
-          wv.y = fmaf(wv.y, decay, -ls * xv.y);
-          wv.z = fmaf(wv.z, decay, -ls * xv.z);
-          wv.w = fmaf(wv.w, decay, -ls * xv.w);
-          store_nt4(reinterpret_cast<float *>(pw), wv);
-        }
+#pragma unroll
+      for (int q = 0; q < KB; ++q) {
+        if (!pw[q]) continue;
+        float4 o;
+        o.x = fmaf(wv[q].x, decay, -ls * xv[q].x);
+        o.y = fmaf(wv[q].y, decay, -ls * xv[q].y);
+        o.z = fmaf(wv[q].z, decay, -ls * xv[q].z);
+        o.w = fmaf(wv[q].w, decay, -ls * xv[q].w);
+        store_nt4(pw[q], o);
       }
     }
     __syncthreads();
