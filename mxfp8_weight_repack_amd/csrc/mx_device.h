@@ -1,5 +1,5 @@
-// mx_device.h -- device-side MXFP8 pieces shared by the G kernels and the
-// Newton-Schulz epilogue that fuses G into f2.
+// mx_device.h -- device-side MXFP8 pieces of the G kernels (1 x 32 blocks,
+// with or without AdamW fused in front).
 //
 // A lane owns 4 consecutive elements of a row and 8 consecutive lanes (aligned
 // to 8) one 32-element block along K.  The block amax is an integer max of the
