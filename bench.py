@@ -50,6 +50,8 @@ def parse():
                     help="scale layout (default: the workload's own); block32x32 = one scale per 32x32 block")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--g", choices=["mxfp8", "bf16"], default="mxfp8",
+                    help="G on the runtime weights: MXFP8 requant (default) or a bfloat16 cast")
     ap.add_argument("--cpu-budget", type=float, default=25.0, help="seconds of oracle work to aim for")
     ap.add_argument("--part", choices=["step", "rs"], default="step",
                     help="step: the update step (default); rs: the reduce-scatter tail on the workload's "
@@ -229,7 +231,10 @@ def main():
         return bench_rs(args, wl)
     w0, g0 = wl.arrays()
     layout = args.layout or wl.scale_layout
-    plan = sh.Plan(wl.nodes, wl.root_numel, layout=layout)
+    nodes = wl.nodes
+    if args.g == "bf16":                      # every G region becomes a bfloat16 cast
+        nodes = [dict(nd, quantize="bf16") if nd["quantize"] else nd for nd in nodes]
+    plan = sh.Plan(nodes, wl.root_numel, layout=layout)
     st = plan.stats()
     w = torch.from_numpy(w0).to(dev)
     g = torch.from_numpy(g0).to(dev)
@@ -239,7 +244,8 @@ def main():
     scales = torch.zeros(st["scale_bytes"], dtype=torch.uint8, device=dev)
     ws_bytes = max(int(st["workspace_bytes"]), 256)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    bufs = sh.buffers(w, g, m, v, codes, scales)
+    w16 = torch.empty(wl.root_numel, dtype=torch.bfloat16, device=dev) if args.g == "bf16" else None
+    bufs = sh.buffers(w, g, m, v, codes, scales, w_bf16=w16)
     mhp, ahp = sh.muon_hp(), sh.adamw_hp()
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
@@ -327,6 +333,12 @@ def main():
         repack = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": gbs / HBM_PEAK_GBS, "bytes_per_step": byts,
                   "traffic": measured_traffic(wl.name, "repack")}
+    cast = None
+    if prof["cast_bf16"][0] > 0:          # G as a bfloat16 cast: 4 (read w) + 2 (write) bytes per element
+        byts = 6.0 * st["cast_elems"]
+        gbs = byts * args.steps / (prof["cast_bf16"][0] / 1e3) / 1e9
+        cast = {"bound": "hbm", "kernel": "k_cast_bf16", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS, "bytes_per_step": byts}
     out = {
         "metric": METRIC, "value": value, "unit": "params/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms,
@@ -336,8 +348,8 @@ def main():
         "config": {"workload": wl.name, "params": wl.params, "root_numel": wl.root_numel,
                    "muon_units": st["n_muon_units"], "adamw_units": st["n_adamw_units"],
                    "ns_groups": [[gi["r"], gi["c"], gi["n_units"]] for gi in plan.groups()],
-                   "scale_layout": layout, "ns_tflop_per_step": st["ns_flops"] / 1e12},
-        "roofline": roofline, "repack_roofline": repack, "components": components,
+                   "scale_layout": layout, "g": args.g, "ns_tflop_per_step": st["ns_flops"] / 1e12},
+        "roofline": roofline, "repack_roofline": repack, "cast_roofline": cast, "components": components,
         "graph_ms_per_step": graph_ms,
     }
     out["env"] = run_env(torch, wl)
