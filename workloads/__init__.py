@@ -204,6 +204,21 @@ def mixed_tiles(cid=101, name="odd multiples of 128 (256-tile blocks with 128-ti
     return _finish(cid, name, t, "rowmajor")
 
 
+def random_units(cid=102, n=6, name="random Muon shapes"):
+    """n Muon units of random shapes (rows, cols in [2, 640], cols a multiple
+    of 4, drawn on the structure stream), wide and tall, each its own region,
+    plus one AdamW vector: shapes that land anywhere relative to the 128- and
+    256-tile grids."""
+    r = rng(cid, 2)
+    t = _Tree()
+    for _ in range(n):
+        rows = int(r.integers(2, 641))
+        cols = int(r.integers(1, 161)) * 4
+        t.region(rows, cols, unit=True, opt="muon")
+    t.region(1, 100, unit=True, opt="adamw")
+    return _finish(cid, name, t, "rowmajor")
+
+
 def _finish(cid, name, t, layout):
     params = 0
     for n in t.nodes:
