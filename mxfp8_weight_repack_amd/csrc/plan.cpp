@@ -255,16 +255,33 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
   std::vector<size_t> order(p.groups.size());
   for (size_t i = 0; i < order.size(); ++i) order[i] = i;
   std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) { return cost[x] > cost[y]; });
-  p.n_lanes = (int)std::min<size_t>(std::max<size_t>(p.groups.size(), 1), kMaxLanes);
+  // The largest group takes the caller's stream (lane 0); the others are dealt,
+  // largest first, to as few side streams as keep each side stream's load within
+  // lane 0's: side work that finishes inside the critical path anyway, with
+  // fewer side kernels contending for the CUs at once (d=2048 block: the O
+  // projection and the 24 heads on one side stream, 2.44 ms per step against
+  // 2.47 on two).  Once kMaxLanes are open, the least-loaded lane takes the rest.
   p.group_lane.assign(p.groups.size(), 0);
+  p.n_lanes = 1;
   {
-    std::vector<double> load(p.n_lanes, 0.0);
-    for (size_t k = 0; k < order.size(); ++k) {
-      int best = 0;
+    std::vector<double> load(kMaxLanes, 0.0);
+    if (!order.empty()) load[0] = cost[order[0]];
+    for (size_t k = 1; k < order.size(); ++k) {
+      const double c = cost[order[k]];
+      int best = -1;
       for (int l = 1; l < p.n_lanes; ++l)
-        if (load[l] < load[best]) best = l;
+        if (load[l] + c <= load[0] && (best < 0 || load[l] < load[best])) best = l;
+      if (best < 0) {
+        if (p.n_lanes < kMaxLanes) {
+          best = p.n_lanes++;
+        } else {
+          best = 0;
+          for (int l = 1; l < p.n_lanes; ++l)
+            if (load[l] < load[best]) best = l;
+        }
+      }
       p.group_lane[order[k]] = best;
-      load[best] += cost[order[k]];
+      load[best] += c;
     }
   }
   // per-lane, per-stage tile tables: symmetric Gram/poly take tm <= tn; longest K first
