@@ -236,12 +236,16 @@ void sshdp_plan_destroy(sshdp_plan *plan);
  * batched bf16 MFMA GEMMs per group) and f2 (main-weight update, fused into the
  * last Newton-Schulz product) [SS-HSDP §3.1 EG1, §4.1].  Reads grad, mom,
  * w_main; writes mom, w_main.  `workspace`: device memory of at least
- * stats.workspace_bytes, 256-byte aligned; its contents on entry are ignored. */
+ * stats.workspace_bytes, 256-byte aligned; its contents on entry are ignored.
+ * Errors (nothing is launched): ARG (null plan/bufs/hp/grad/mom/w_main, or the
+ * current device is not the plan's), STATE (host-only plan), ALIGN, WORKSPACE
+ * (null or too small); HIP if a launch fails. */
 int sshdp_update_muon(const sshdp_plan *plan, const sshdp_buffers *bufs, const sshdp_muon_hp *hp,
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /* F for every AdamW unit at step `step` (>= 1, caller-owned, same for all
- * units).  Reads grad, mom, adam_v, w_main; writes mom, adam_v, w_main. */
+ * units).  Reads grad, mom, adam_v, w_main; writes mom, adam_v, w_main.
+ * Errors: ARG (null pointers, step < 1, wrong device), STATE, ALIGN; HIP. */
 int sshdp_update_adamw(const sshdp_plan *plan, const sshdp_buffers *bufs, const sshdp_adamw_hp *hp,
                        int64_t step, void *stream);
 
@@ -250,13 +254,16 @@ int sshdp_update_adamw(const sshdp_plan *plan, const sshdp_buffers *bufs, const 
  * [-127,127]; all-zero block -> -127), scale byte e+127 at the layout's index,
  * codes = E4M3FN round-to-nearest-even of x*2^-e, written at the elements' own
  * offsets.  A block holding NaN/Inf gets scale 0xFF and codes 0x7F.  Reads
- * w_main; writes codes and scales. */
+ * w_main; writes codes and scales.  A plan without MXFP8 regions returns OK at
+ * once.  Errors: ARG (null pointers, wrong device), STATE, ALIGN (w_main or
+ * codes); HIP. */
 int sshdp_requant_mxfp8(const sshdp_plan *plan, const float *w_main, uint8_t *codes, uint8_t *scales,
                         void *stream);
 
 /* G for every BF16 region [SS-HSDP §2.1]: w_bf16 = bfloat16(w_main), round to
  * nearest even, at the elements' own offsets (a runtime view of a BF16 weight
- * is the same sub-range of w_bf16).  Reads w_main; writes w_bf16. */
+ * is the same sub-range of w_bf16).  Reads w_main; writes w_bf16.  A plan
+ * without BF16 regions returns OK at once.  Errors: ARG, STATE, ALIGN; HIP. */
 int sshdp_cast_bf16(const sshdp_plan *plan, const float *w_main, uint16_t *w_bf16, void *stream);
 
 /* The reduce-scatter tail [SS-HSDP §4.3 "Reduce-Scatter", Figure 5(e)]: within
@@ -295,7 +302,10 @@ int sshdp_rs_accumulate(const void *const *inputs, int32_t n_inputs, int32_t in_
 /* The whole update phase in order [SS-HSDP §3.4 "Update"]: Muon F, AdamW F
  * (fused with G for MXFP8 regions holding only AdamW units), then G for the
  * remaining MXFP8 regions and the BF16 regions.  Equivalent to
- * sshdp_update_muon; sshdp_update_adamw; sshdp_requant_mxfp8; sshdp_cast_bf16. */
+ * sshdp_update_muon; sshdp_update_adamw; sshdp_requant_mxfp8; sshdp_cast_bf16.
+ * Every argument the plan's parts need is checked before anything is launched
+ * (the errors of those calls); mh may be NULL for a plan without Muon units
+ * and ah for one without AdamW units. */
 int sshdp_update_step(const sshdp_plan *plan, const sshdp_buffers *bufs, const sshdp_muon_hp *mh,
                       const sshdp_adamw_hp *ah, int64_t step, void *workspace, size_t workspace_bytes,
                       void *stream);
