@@ -261,8 +261,10 @@ int sshdp_update_step(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_m
 int sshdp_gemm_bf16_nt(const void *P, const void *Q, const void *D, void *O, void *OT, int32_t M, int32_t N,
                        int32_t K, int32_t batch, float alpha, float beta, int32_t tile, void *stream) {
   if (!P || !Q || !O || M <= 0 || N <= 0 || K <= 0 || batch <= 0) return SSHDP_ERR_ARG;
-  if (tile != 128 && tile != 256) return SSHDP_ERR_ARG;
-  if (M % tile || N % tile || K % 64) return SSHDP_ERR_SCHEMA;
+  if (tile != 128 && tile != 256 && tile != 1281 && tile != 2561) return SSHDP_ERR_ARG;
+  const int tt = tile == 1281 ? 128 : tile == 2561 ? 256 : tile;
+  if (M % tt || N % tt || K % 64) return SSHDP_ERR_SCHEMA;
+  if (tt != tile && (D || M != N)) return SSHDP_ERR_ARG;
   if (!aligned16(P) || !aligned16(Q) || (D && !aligned16(D)) || !aligned16(O) || (OT && !aligned16(OT)))
     return SSHDP_ERR_ALIGN;
   return hip_status(launch_gemm_raw(P, Q, D, O, OT, M, N, K, batch, alpha, D ? beta : 0.f, tile,

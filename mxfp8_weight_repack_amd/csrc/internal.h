@@ -30,8 +30,8 @@ struct MuonUnit {
   int32_t tile_begin;   // f0 tiles [tile_begin, tile_end) -> norm partials
   int32_t tile_end;
   int32_t Rp, Cp;       // padded original dims: the unit's own layout is Rp x Cp
-  int64_t ws_orig;      // workspace byte offset of bf16 u in the unit's own layout (Rp x Cp)
-  int64_t ws_trans;     // ... and of its transpose (Cp x Rp)
+  int64_t ws_orig;      // workspace byte offset of bf16 u in the unit's own layout (Rp x Cp), -1: not stored
+  int64_t ws_trans;     // ... and of its transpose (Cp x Rp), -1: not stored
   float upd_scale;      // update scale (scale mode) of f2
   int32_t pad_;
 };
@@ -48,6 +48,7 @@ struct Group {
   // 256-tile regions (multiples of 256; 0 = none); the rest of each product in 128-tiles:
   // Gram/poly rows and columns [0, g256), update rows [0, u256r) x columns [0, u256c)
   int32_t g256, u256r, u256c;
+  int32_t km;           // Gram from X^T with transposing LDS reads (128-tile Gram groups)
   int32_t unit_base;    // first MuonUnit of the group in the device table
   size_t off_x, off_xt0, off_xt1, off_a, off_b;   // workspace byte offsets
 };
@@ -56,6 +57,8 @@ struct Group {
 struct NsGroupDev {
   int64_t off_x, off_xt0, off_xt1, off_a, off_b;   // workspace byte offsets
   int32_t r_pad, c_pad, unit_base, n;
+  int32_t km;           // Gram read from X^T (K-major); X itself is never stored
+  int32_t pad_;
 };
 
 // One macro tile of one stage: group, unit within the group, tile row/column.

@@ -66,8 +66,9 @@ __global__ __launch_bounds__(256) void k_f0(const MuonUnit *__restrict__ units, 
   const int t = threadIdx.x;
   const int cq = t & 15, r0 = t >> 4;
   const int col = tl.tc * T + cq * 4;
-  uint16_t *orig = reinterpret_cast<uint16_t *>(ws + u.ws_orig);
-  uint16_t *trans = reinterpret_cast<uint16_t *>(ws + u.ws_trans);
+  // either copy may be absent (-1): groups whose Gram reads X^T keep only u^T
+  uint16_t *orig = u.ws_orig >= 0 ? reinterpret_cast<uint16_t *>(ws + u.ws_orig) : nullptr;
+  uint16_t *trans = u.ws_trans >= 0 ? reinterpret_cast<uint16_t *>(ws + u.ws_trans) : nullptr;
   // all eight 16-byte loads first, so each lane has them in flight together
   float4 gvs[4], mvs[4];
 #pragma unroll
@@ -114,9 +115,11 @@ __global__ __launch_bounds__(256) void k_f0(const MuonUnit *__restrict__ units, 
     uint2 packed;
     packed.x = b[0] | (b[1] << 16);
     packed.y = b[2] | (b[3] << 16);
-    *reinterpret_cast<uint2 *>(orig + (int64_t)row * u.Cp + col) = packed;
+    if (orig) *reinterpret_cast<uint2 *>(orig + (int64_t)row * u.Cp + col) = packed;
+    if (trans) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lds[(cq * 4 + j) * PITCH + lr] = (uint16_t)b[j];
+      for (int j = 0; j < 4; ++j) lds[(cq * 4 + j) * PITCH + lr] = (uint16_t)b[j];
+    }
   }
   // sum of squares: wave butterfly, then the 4 waves in order (deterministic)
 #pragma unroll
@@ -125,6 +128,7 @@ __global__ __launch_bounds__(256) void k_f0(const MuonUnit *__restrict__ units, 
   __syncthreads();
   if (t == 0) partials[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
   // transposed tile: row c of the transpose = column c of the tile
+  if (!trans) return;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int c = (t >> 3) + 32 * pass, seg = t & 7;

@@ -18,6 +18,10 @@
 //           X^T read back from the Q operand's LDS stages (no extra memory
 //           read); the epilogue writes X' and X'^T, the operands of the next
 //           step (no transpose pass)
+// Groups whose Gram runs in 128-tiles read it from X^T instead ("K-major":
+// both operands staged k-row by k-row and turned into MFMA fragments by
+// ds_read_b64_tr_b16 pairs), so their update stores X'^T alone and f0 stores
+// u^T alone.
 // A and B are symmetric: only tiles with tm <= tn are computed and each
 // off-diagonal tile is also stored mirrored.  The normalisation is folded into
 // the first step's scalars: with s = 1/(||u|| + eps), A0 = s^2 u u^T and
@@ -115,9 +119,22 @@ __device__ __forceinline__ void store_nt4(float *p, const float4 &v) {
 // the K steps covering [dk0, dk0 + TM).  While a stage is resident, the waves
 // whose rows it covers add dscale * D into their accumulators straight from
 // LDS, and the epilogue reads nothing more from memory.
-template <class C, bool CAPD = false>
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// K-major stage rows (one k, T columns): 16-byte chunk c of row k sits at
+// physical chunk c ^ km_swz(k), so the four rows a transposing read touches
+// together fall on distinct bank groups.
+__device__ __forceinline__ int km_swz(int k) { return (k & 3) << 2; }
+
+// KM: both operands K-major (P stored [K][...] with row pitch ld elements, gP at
+// element (k = 0, first row of the tile), likewise Q): the Gram read from X^T.
+// Fragments come from ds_read_b64_tr_b16 pairs (each gives a lane 4 k of its row).
+template <class C, bool CAPD = false, bool KM = false>
 __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_t K, char *smem,
-                                          f32x16_t (&acc)[C::MBM][C::MBN], int dk0 = 0, float dscale = 0.f) {
+                                          f32x16_t (&acc)[C::MBM][C::MBN], int dk0 = 0, float dscale = 0.f,
+                                          int64_t ld = 0) {
+  static_assert(!(CAPD && KM), "the added term is read from an NT stage");
   constexpr int MBM = C::MBM, MBN = C::MBN, NW = C::NW, BK = C::BK, RB = C::RB, CPR = C::CPR, RPI = C::RPI;
   constexpr int NST = C::NST;
   const int t = threadIdx.x, lane = t & 63;
@@ -132,10 +149,17 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
   const int drow = RPI * wave + lane / CPR;
   const int dchunk = (lane % CPR) ^ swz<BK>(drow);   // rows drow + RPI*NW*i share the swizzle
   const int voff = (drow * (int)K + dchunk * 8) * 2;
-  const __amdgpu_buffer_rsrc_t rP =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(gP), 0, (int)(C::TM * K * 2), kBufWord3);
-  const __amdgpu_buffer_rsrc_t rQ =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(gQ), 0, (int)(C::TN * K * 2), kBufWord3);
+  const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char *>(gP), 0, KM ? (int)(((K - 1) * ld + C::TM) * 2) : (int)(C::TM * K * 2), kBufWord3);
+  const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char *>(gQ), 0, KM ? (int)(((K - 1) * ld + C::TN) * 2) : (int)(C::TN * K * 2), kBufWord3);
+  // K-major DMA: a load fills RK = 1024 / (2 T) whole rows (k) of T columns; load i
+  // of wave w fills rows RK*(NW*i + w) ..; the row's swizzle depends on k % 4 only
+  constexpr int CKA = C::TM / 8, CKB = C::TN / 8;                  // 16-byte chunks per K-major row
+  constexpr int RKA = 64 / CKA, RKB = 64 / CKB;                    // rows per load
+  const int kra = RKA * wave + lane / CKA, krb = RKB * wave + lane / CKB;
+  const int voffa = (int)(kra * ld * 2) + (((lane % CKA) ^ km_swz(kra)) << 4);
+  const int voffb = (int)(krb * ld * 2) + (((lane % CKB) ^ km_swz(krb)) << 4);
 
   // fragment reads: lane holds row (lane & 31) of a 32-row block, logical chunk 2 kk + (lane >> 5)
   const int lrow = lane & 31;
@@ -154,19 +178,51 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
   auto dma_p = [&](int stage, int k0) __attribute__((always_inline)) {
     char *sa = smem + stage * C::STAGE + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < C::NIA; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (__attribute__((address_space(3))) void *)(sa + i * NW * 1024),
-                                               16, voff, (i * RPI * NW * (int)K + k0) * 2, 0, 0);
+    for (int i = 0; i < C::NIA; ++i) {
+      if (KM)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (__attribute__((address_space(3))) void *)(sa + i * NW * 1024),
+                                                 16, voffa, (int)((k0 + i * RKA * NW) * ld * 2), 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (__attribute__((address_space(3))) void *)(sa + i * NW * 1024),
+                                                 16, voff, (i * RPI * NW * (int)K + k0) * 2, 0, 0);
+    }
   };
   auto dma_q = [&](int stage, int k0) __attribute__((always_inline)) {
     char *sa = smem + stage * C::STAGE + C::SEGA + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < C::NIB; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (__attribute__((address_space(3))) void *)(sa + i * NW * 1024),
-                                               16, voff, (i * RPI * NW * (int)K + k0) * 2, 0, 0);
+    for (int i = 0; i < C::NIB; ++i) {
+      if (KM)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (__attribute__((address_space(3))) void *)(sa + i * NW * 1024),
+                                                 16, voffb, (int)((k0 + i * RKB * NW) * ld * 2), 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (__attribute__((address_space(3))) void *)(sa + i * NW * 1024),
+                                                 16, voff, (i * RPI * NW * (int)K + k0) * 2, 0, 0);
+    }
   };
   bf16x8_t fa0[MBM], fb0[MBN], fa1[MBM], fb1[MBN];
+  // K-major fragment: in each 16-lane group, source lane s reads 4 columns of row
+  // k0 + s/4; the transposing read hands lane i of the group column i at rows
+  // k0 .. k0+3.  Lane l: row (in the 32-row block) l % 32, k = 16 kk + 8 (l/32) + 0..7
+  // from two reads (k0 and k0 + 4).
+  const int tk = 8 * (lane >> 5) + ((lane & 15) >> 2);             // k of this lane's read, slice-relative
+  const int tm = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);          // first column it reads, block-relative
+  const int tsw = km_swz(tk);                                       // = 4 * ((lane & 15) >> 2)
+  auto ldtr = [&](const char *seg, int rowbytes, int col, int kk) __attribute__((always_inline)) {
+    const char *base = seg + (16 * kk + tk) * rowbytes + (col & 7) * 2;
+    const int c = col >> 3;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(base + ((c ^ tsw) << 4)));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(base + 4 * rowbytes + ((c ^ tsw) << 4)));
+    const i16x4_t v[2] = {lo, hi};
+    return *reinterpret_cast<const bf16x8_t *>(v);
+  };
   auto ldfrag = [&](const char *sa, int kk, bf16x8_t(&fa_)[MBM], bf16x8_t(&fb_)[MBN]) __attribute__((always_inline)) {
+    if (KM) {
+#pragma unroll
+      for (int i = 0; i < MBM; ++i) fa_[i] = ldtr(sa, C::TM * 2, wm * C::WTM + i * 32 + tm, kk);
+#pragma unroll
+      for (int j = 0; j < MBN; ++j) fb_[j] = ldtr(sa + C::SEGA, C::TN * 2, wn * C::WTN + j * 32 + tm, kk);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < MBM; ++i) fa_[i] = *reinterpret_cast<const bf16x8_t *>(sa + ra + i * 32 * RB + cofs[kk]);
 #pragma unroll
@@ -185,7 +241,7 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < nr) __builtin_amdgcn_sched_group_barrier(0x100, KM ? 2 : 1, 0);
       if (i < nv) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
   };
@@ -310,7 +366,8 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
 }
 
 // Epilogue of a TM x TN product: x = alpha*acc + beta*D, rounded to bf16,
-// stored row-major to O (leading dim ldo) and, if OT, transposed to OT[col*ldt + row].
+// stored row-major to O (leading dim ldo; skipped if O is null) and, if OT,
+// transposed to OT[col*ldt + row].
 // D is read through its transpose DT (DT[col*lddt + row] = D[row][col]): element
 // (m, n) of a 32x32 MFMA block sits in lane n + 32*((m/4)%2), register
 // (m/8)*4 + m%4, so a lane holds 4 consecutive rows of one column and the D^T
@@ -350,20 +407,24 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[C::MBM][C::MBN]
         }
         const uint32_t h01 = pk_bf16(x[0], x[1]), h23 = pk_bf16(x[2], x[3]);
         hp[i][j][g4] = make_uint2(h01, h23);
-        lt[(lr0 + 0) * LP + lc] = (uint16_t)h01;
-        lt[(lr0 + 1) * LP + lc] = (uint16_t)(h01 >> 16);
-        lt[(lr0 + 2) * LP + lc] = (uint16_t)h23;
-        lt[(lr0 + 3) * LP + lc] = (uint16_t)(h23 >> 16);
+        if (O) {
+          lt[(lr0 + 0) * LP + lc] = (uint16_t)h01;
+          lt[(lr0 + 1) * LP + lc] = (uint16_t)(h01 >> 16);
+          lt[(lr0 + 2) * LP + lc] = (uint16_t)h23;
+          lt[(lr0 + 3) * LP + lc] = (uint16_t)(h23 >> 16);
+        }
       }
     }
   }
-  __syncthreads();
-  constexpr int CH = C::TN / 8;                      // 16-byte chunks per row
+  if (O) {
+    __syncthreads();
+    constexpr int CH = C::TN / 8;                    // 16-byte chunks per row
 #pragma unroll
-  for (int k = 0; k < C::TM * CH / C::NT; ++k) {
-    const int id = t + C::NT * k, row = id / CH, ch = id - row * CH;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(&lt[row * LP + ch * 8]);
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(O + (int64_t)(r0 + row) * ldo + c0 + ch * 8));
+    for (int k = 0; k < C::TM * CH / C::NT; ++k) {
+      const int id = t + C::NT * k, row = id / CH, ch = id - row * CH;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(&lt[row * LP + ch * 8]);
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(O + (int64_t)(r0 + row) * ldo + c0 + ch * 8));
+    }
   }
   if (!OT) return;
   __syncthreads();
@@ -509,8 +570,15 @@ __global__ __launch_bounds__(C::NT, C::NT == 256 ? 2 : 1) void k_ns(NsArgs a) {
   const int r0 = tl.tm * TILE, c0 = tl.tn * TILE;
   f32x16_t acc[C::MBM][C::MBN];
   if (STAGE == 0) {
-    gemm_core<C>(reinterpret_cast<const char *>(X + r0 * cp), reinterpret_cast<const char *>(X + c0 * cp), cp,
-                    smem, acc);
+    if (g.km) {
+      // from X^T (c_pad x r_pad): the tile's rows and columns are X^T columns
+      const uint16_t *XTc = (a.iter & 1) ? XT1 : XT0;
+      gemm_core<C, false, true>(reinterpret_cast<const char *>(XTc + r0), reinterpret_cast<const char *>(XTc + c0),
+                                cp, smem, acc, 0, 0.f, rp);
+    } else {
+      gemm_core<C>(reinterpret_cast<const char *>(X + r0 * cp), reinterpret_cast<const char *>(X + c0 * cp), cp,
+                   smem, acc);
+    }
     const float al = a.iter == 0 ? s * s : 1.f;
     store_tile<C>(acc, al, 0.f, nullptr, 0, A, rp, tl.tm != tl.tn ? A : nullptr, rp, r0, c0, smem);
   } else if (STAGE == 1) {
@@ -526,7 +594,7 @@ __global__ __launch_bounds__(C::NT, C::NT == 256 ? 2 : 1) void k_ns(NsArgs a) {
     if (STAGE == 2) {
       gemm_core<C, true>(reinterpret_cast<const char *>(B + r0 * rp),
                          reinterpret_cast<const char *>(XTc + c0 * rp), rp, smem, acc, r0, a.ca);
-      store_tile<C>(acc, al, 0.f, nullptr, 0, X, cp, XTn, rp, r0, c0, smem);
+      store_tile<C>(acc, al, 0.f, nullptr, 0, g.km ? nullptr : X, cp, XTn, rp, r0, c0, smem);
     } else {
       if (!zero)
         gemm_core<C, true>(reinterpret_cast<const char *>(B + r0 * rp),
@@ -558,6 +626,23 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm_raw(RawArgs a) {
   // the raw entry takes D^T (N x M), the layout the update product reads X in
   store_tile<C>(acc, a.alpha, a.beta, a.D ? a.D + b * M * N : nullptr, M, a.O + b * M * N, N,
                 a.OT ? a.OT + b * M * N : nullptr, M, tm * C::TM, tn * C::TN, smem);
+}
+
+// Raw K-major ("TN") contraction for tests: O[b] = alpha P[b]^T Q[b] with P[b]
+// K x M and Q[b] K x N row-major (the Gram read from X^T).
+template <class C>
+__global__ __launch_bounds__(C::NT, 1) void k_gemm_raw_km(RawArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+  const int b = blockIdx.y;
+  int tm, tn;
+  xcd_tile((int)blockIdx.x, a.M / C::TM, a.N / C::TN, &tm, &tn);
+  const int64_t M = a.M, N = a.N, K = a.K;
+  f32x16_t acc[C::MBM][C::MBN];
+  gemm_core<C, false, true>(reinterpret_cast<const char *>(a.P + b * K * M + (int64_t)tm * C::TM),
+                            reinterpret_cast<const char *>(a.Q + b * K * N + (int64_t)tn * C::TN), K, smem, acc, 0,
+                            0.f, M);
+  store_tile<C>(acc, a.alpha, 0.f, nullptr, 0, a.O + b * M * N, N, a.OT ? a.OT + b * M * N : nullptr, M,
+                tm * C::TM, tn * C::TN, smem);
 }
 
 using CSmall = Cfg<kNsSmall, kNsSmall, 2, 2>;   // 4 waves, two workgroups per CU
@@ -624,6 +709,12 @@ hipError_t launch_gemm_raw(const void *P, const void *Q, const void *D, void *O,
   } else if (tile == 256) {
     using C = CLarge;
     hipLaunchKernelGGL(k_gemm_raw<C>, dim3((unsigned)((M / 256) * (N / 256)), (unsigned)batch), dim3(C::NT), 0, s, a);
+  } else if (tile == 1281) {   // K-major operands (M must equal N for the shared pitch rule below)
+    using C = CSmall;
+    hipLaunchKernelGGL(k_gemm_raw_km<C>, dim3((unsigned)((M / 128) * (N / 128)), (unsigned)batch), dim3(C::NT), 0, s, a);
+  } else if (tile == 2561) {
+    using C = CLarge;
+    hipLaunchKernelGGL(k_gemm_raw_km<C>, dim3((unsigned)((M / 256) * (N / 256)), (unsigned)batch), dim3(C::NT), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }

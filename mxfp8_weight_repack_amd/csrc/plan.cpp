@@ -191,6 +191,12 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
       g.u256r = upd ? (int32_t)(R2 * kNsLarge) : 0;
       g.u256c = upd ? (int32_t)(C2 * kNsLarge) : 0;
       g.g256 = gram ? (int32_t)(R2 * kNsLarge) : 0;
+      // 128-tile Grams read X^T through transposing LDS reads, so the update stores X^T
+      // only (and f0 only u^T): on those shapes the transposing read costs the Gram
+      // 4-10% while the single-output epilogue saves ~8% of every update, more where
+      // the update's K is short (MoE r = 1408).  256-tile Grams lose ~10% that way and
+      // keep the NT form.
+      g.km = g.g256 == 0 ? 1 : 0;
     }
     g.n = (int32_t)kv.second.size();
     g.unit_base = (int32_t)p.munits.size();
@@ -227,7 +233,7 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
   off = round_up(off + p.f0tiles.size() * sizeof(float), kAlign);
   for (Group &g : p.groups) {
     const size_t xs = (size_t)g.n * g.r_pad * g.c_pad * 2, as = (size_t)g.n * g.r_pad * g.r_pad * 2;
-    g.off_x = off;   off = round_up(off + xs, kAlign);
+    g.off_x = off;   off = round_up(off + (g.km ? 0 : xs), kAlign);   // X is not stored for K-major Grams
     g.off_xt0 = off; off = round_up(off + xs, kAlign);
     g.off_xt1 = off; off = round_up(off + xs, kAlign);
     g.off_a = off;   off = round_up(off + as, kAlign);
@@ -238,6 +244,7 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
       const int64_t ut = (int64_t)g.off_xt0 + (int64_t)k * g.r_pad * g.c_pad * 2;
       u.ws_orig = u.tall ? ut : ux;     // a tall unit's own layout is X^T
       u.ws_trans = u.tall ? ux : ut;
+      if (g.km) (u.tall ? u.ws_trans : u.ws_orig) = -1;   // only X^T is stored
     }
   }
   p.ws_bytes = off;
@@ -288,7 +295,7 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
   for (size_t gi = 0; gi < p.groups.size(); ++gi) {
     const Group &g = p.groups[gi];
     p.ns_groups.push_back({(int64_t)g.off_x, (int64_t)g.off_xt0, (int64_t)g.off_xt1, (int64_t)g.off_a,
-                           (int64_t)g.off_b, g.r_pad, g.c_pad, g.unit_base, g.n});
+                           (int64_t)g.off_b, g.r_pad, g.c_pad, g.unit_base, g.n, g.km, 0});
     const int ln = p.group_lane[gi];
     const int n2 = g.g256 / kNsLarge, n1 = g.r_pad / kNsSmall, s1 = g.g256 / kNsSmall;
     const int ur2 = g.u256r / kNsLarge, uc2 = g.u256c / kNsLarge;

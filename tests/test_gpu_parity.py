@@ -66,6 +66,30 @@ def test_gemm_nt_against_fp64(tile, M, N, K, batch):
     assert torch.equal(OT, O.transpose(1, 2).contiguous())
 
 
+@pytest.mark.parametrize("tile,M,N,K,batch", [(1281, 128, 128, 192, 2), (1281, 384, 384, 640, 3),
+                                              (2561, 256, 256, 320, 2), (2561, 512, 512, 128, 1)])
+def test_gemm_kmajor_against_fp64(tile, M, N, K, batch):
+    """The K-major operand path (transposing LDS reads): O = alpha P^T Q with
+    P K x M and Q K x N row-major, M = N (one row pitch, as for the Gram read
+    from X^T)."""
+    say(f"gemm K-major tile={tile} M={M} N={N} K={K} batch={batch}")
+    r = np.random.default_rng(M * 7 + N + K + tile)
+    P = r.standard_normal((batch, K, M)).astype(np.float32)
+    Q = r.standard_normal((batch, K, N)).astype(np.float32)
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).cuda()
+    O = torch.zeros(batch, M, N, dtype=torch.bfloat16, device="cuda")
+    OT = torch.zeros(batch, N, M, dtype=torch.bfloat16, device="cuda")
+    sh.gemm_bf16_nt(bf(P), bf(Q), None, O, OT, M, N, K, batch, 0.75, 0.0, tile,
+                    torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref = 0.75 * np.einsum("bki,bkj->bij", _bf16_host(P), _bf16_host(Q))
+    got = O.float().cpu().numpy().astype(np.float64)
+    scale = np.sqrt(K) + 2.0
+    assert np.max(np.abs(got - ref)) <= 2 ** -7 * scale * 1.5 + 1e-3
+    assert rel_fro(got, ref) < 4e-3
+    assert torch.equal(OT, O.transpose(1, 2).contiguous())
+
+
 # ----------------------------------------------------------------------------- G alone
 def _specials(w, wl):
     """Plant NaN/Inf/-0/subnormal/zero blocks inside the quantised regions."""
