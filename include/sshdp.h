@@ -315,7 +315,9 @@ int sshdp_update_step(const sshdp_plan *plan, const sshdp_buffers *bufs, const s
  * with P[b] M x K, Q[b] N x K, O[b] M x N (bf16, row-major, dense, batch strides
  * M*K, N*K, M*N).  D is passed TRANSPOSED, DT[b] N x M (the layout in which the
  * update product reads X), or NULL (beta ignored); OT (optional) receives
- * O[b]^T (N x M).  M, N must be multiples of `tile` (128 or 256), K of 64. */
+ * O[b]^T (N x M).  M, N must be multiples of `tile` (128 or 256), K of 64.
+ * tile 1281 / 2561: the same 128 / 256 tiles with both operands K-major (the
+ * Gram read from X^T): P[b] K x M, Q[b] K x N row-major, M == N, D NULL. */
 int sshdp_gemm_bf16_nt(const void *P, const void *Q, const void *D, void *O, void *OT, int32_t M,
                        int32_t N, int32_t K, int32_t batch, float alpha, float beta, int32_t tile,
                        void *stream);
