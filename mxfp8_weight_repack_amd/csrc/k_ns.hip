@@ -135,6 +135,7 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
                                           f32x16_t (&acc)[C::MBM][C::MBN], int dk0 = 0, float dscale = 0.f,
                                           int64_t ld = 0) {
   static_assert(!(CAPD && KM), "the added term is read from an NT stage");
+  static_assert(!KM || (C::BK == 64 && C::TM % 32 == 0 && C::TN % 32 == 0), "K-major stages: 64 k-rows");
   constexpr int MBM = C::MBM, MBN = C::MBN, NW = C::NW, BK = C::BK, RB = C::RB, CPR = C::CPR, RPI = C::RPI;
   constexpr int NST = C::NST;
   const int t = threadIdx.x, lane = t & 63;
