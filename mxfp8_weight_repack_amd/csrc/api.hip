@@ -65,14 +65,16 @@ int run_muon(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_muon_hp *h
   if (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) return SSHDP_ERR_ALIGN;
   char *w = static_cast<char *>(ws);
   hipError_t e;
+  // lane 0 (the caller's stream): f0 and the norms of its own units; the side lanes,
+  // forked after that, run their f0 and norms beside lane 0's first Gram
   {
     Prof pr(p, 0, s);
-    e = launch_f0(*p, b->grad, b->mom, hp->momentum, p->opts.nesterov, w, s);
+    e = launch_f0(*p, 0, b->grad, b->mom, hp->momentum, p->opts.nesterov, w, s);
   }
   if (e != hipSuccess) return SSHDP_ERR_HIP;
   {
     Prof pr(p, 1, s);
-    e = launch_norm(*p, w, p->opts.ns_eps, s);
+    e = launch_norm(*p, 0, w, p->opts.ns_eps, s);
   }
   if (e != hipSuccess) return SSHDP_ERR_HIP;
   // Newton-Schulz: lane 0 on the caller's stream, the other lanes on plan-owned
@@ -80,8 +82,17 @@ int run_muon(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_muon_hp *h
   Prof wall(p, 8, s);
   if (p->n_lanes > 1) {
     if (hipEventRecord(p->ev_fork, s) != hipSuccess) return SSHDP_ERR_HIP;
-    for (int ln = 1; ln < p->n_lanes; ++ln)
-      if (hipStreamWaitEvent(p->lane_stream[ln], p->ev_fork, 0) != hipSuccess) return SSHDP_ERR_HIP;
+    for (int ln = 1; ln < p->n_lanes; ++ln) {
+      hipStream_t ls = p->lane_stream[ln];
+      if (hipStreamWaitEvent(ls, p->ev_fork, 0) != hipSuccess) return SSHDP_ERR_HIP;
+      {
+        Prof pr(p, 0, ls);
+        e = launch_f0(*p, ln, b->grad, b->mom, hp->momentum, p->opts.nesterov, w, ls);
+      }
+      if (e != hipSuccess) return SSHDP_ERR_HIP;
+      Prof pr(p, 1, ls);
+      if (launch_norm(*p, ln, w, p->opts.ns_eps, ls) != hipSuccess) return SSHDP_ERR_HIP;
+    }
   }
   const int steps = p->opts.ns_steps;
   for (int it = 0; it < steps; ++it) {

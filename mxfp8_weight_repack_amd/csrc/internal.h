@@ -118,6 +118,7 @@ struct DeviceTables {
   CChunk *cchunks = nullptr;
   NsGroupDev *ns_groups = nullptr;
   NsTile *ns_tiles[kMaxLanes][3][2] = {};   // [lane][stage: Gram, poly, update][tile: 128, 256]
+  int32_t *norm_units = nullptr;
 };
 
 }  // namespace sshdp
@@ -135,6 +136,11 @@ struct sshdp_plan {
   // streams joined back by events); per lane, stage and tile size a tile table, longest K first
   int n_lanes = 1;
   std::vector<int32_t> group_lane;
+  // f0 tiles and the units whose norms they feed, contiguous per lane: lane l owns tiles
+  // [f0_lane[l], f0_lane[l+1]) and units norm_units[norm_lane[l] .. norm_lane[l+1])
+  int32_t f0_lane[sshdp::kMaxLanes + 1] = {};
+  int32_t norm_lane[sshdp::kMaxLanes + 1] = {};
+  std::vector<int32_t> norm_units;
   std::vector<sshdp::NsTile> ns_tiles[sshdp::kMaxLanes][3][2];
   hipStream_t lane_stream[sshdp::kMaxLanes] = {};
   hipEvent_t ev_fork = nullptr, ev_join[sshdp::kMaxLanes] = {};
@@ -160,9 +166,9 @@ struct sshdp_plan {
 
 // Kernel launchers (defined in the .hip translation units).
 namespace sshdp {
-hipError_t launch_f0(const sshdp_plan &p, const float *g, float *m, float mu, int nesterov, char *ws,
+hipError_t launch_f0(const sshdp_plan &p, int lane, const float *g, float *m, float mu, int nesterov, char *ws,
                      hipStream_t s);
-hipError_t launch_norm(const sshdp_plan &p, char *ws, float eps, hipStream_t s);
+hipError_t launch_norm(const sshdp_plan &p, int lane, char *ws, float eps, hipStream_t s);
 // stage: 0 Gram, 1 poly, 2 update, 3 final update (+f2); one launch covers all groups
 hipError_t launch_ns_stage(const sshdp_plan &p, int lane, int stage, int iter, char *ws, float *w_main, float lr,
                            float wd, hipStream_t s);

@@ -138,10 +138,12 @@ __global__ __launch_bounds__(256) void k_f0(const MuonUnit *__restrict__ units, 
 }
 
 // ----------------------------------------------------------------------------- norm
-__global__ __launch_bounds__(256) void k_norm(const MuonUnit *__restrict__ units, const float *__restrict__ partials,
-                                              float *__restrict__ uscale, float eps) {
+__global__ __launch_bounds__(256) void k_norm(const MuonUnit *__restrict__ units, const int32_t *__restrict__ ulist,
+                                              const float *__restrict__ partials, float *__restrict__ uscale,
+                                              float eps) {
   __shared__ float red[4];
-  const MuonUnit u = units[blockIdx.x];
+  const int32_t ui = ulist[blockIdx.x];
+  const MuonUnit u = units[ui];
   float s = 0.f;
   for (int i = u.tile_begin + threadIdx.x; i < u.tile_end; i += 256) s += partials[i];
 #pragma unroll
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(256) void k_norm(const MuonUnit *__restrict__ units
   if (threadIdx.x == 0) {
     const float tot = (red[0] + red[1]) + (red[2] + red[3]);
     // an all-zero unit gets scale 0: its Newton-Schulz products are skipped (direction exactly 0)
-    uscale[blockIdx.x] = tot > 0.f ? 1.0f / (sqrtf(tot) + eps) : 0.f;
+    uscale[ui] = tot > 0.f ? 1.0f / (sqrtf(tot) + eps) : 0.f;
   }
 }
 
@@ -403,17 +405,20 @@ AdamConst adam_const(const sshdp_adamw_hp &hp, int64_t step) {
 
 }  // namespace
 
-hipError_t launch_f0(const sshdp_plan &p, const float *g, float *m, float mu, int nesterov, char *ws,
+hipError_t launch_f0(const sshdp_plan &p, int lane, const float *g, float *m, float mu, int nesterov, char *ws,
                      hipStream_t s) {
-  if (p.f0tiles.empty()) return hipSuccess;
-  hipLaunchKernelGGL(k_f0, dim3((unsigned)p.f0tiles.size()), dim3(256), 0, s, p.d.munits, p.d.f0tiles, g, m, mu,
-                     nesterov, ws, reinterpret_cast<float *>(ws + p.ws_partials));
+  const int32_t b = p.f0_lane[lane], n = p.f0_lane[lane + 1] - b;
+  if (n <= 0) return hipSuccess;
+  // the lane's tiles and their partials (partial i of the launch belongs to tile b + i)
+  hipLaunchKernelGGL(k_f0, dim3((unsigned)n), dim3(256), 0, s, p.d.munits, p.d.f0tiles + b, g, m, mu, nesterov, ws,
+                     reinterpret_cast<float *>(ws + p.ws_partials) + b);
   return hipGetLastError();
 }
 
-hipError_t launch_norm(const sshdp_plan &p, char *ws, float eps, hipStream_t s) {
-  if (p.munits.empty()) return hipSuccess;
-  hipLaunchKernelGGL(k_norm, dim3((unsigned)p.munits.size()), dim3(256), 0, s, p.d.munits,
+hipError_t launch_norm(const sshdp_plan &p, int lane, char *ws, float eps, hipStream_t s) {
+  const int32_t b = p.norm_lane[lane], n = p.norm_lane[lane + 1] - b;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_norm, dim3((unsigned)n), dim3(256), 0, s, p.d.munits, p.d.norm_units + b,
                      reinterpret_cast<const float *>(ws + p.ws_partials), reinterpret_cast<float *>(ws + p.ws_uscale),
                      eps);
   return hipGetLastError();

@@ -291,6 +291,34 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
       load[best] += c;
     }
   }
+  // f0 tiles and norm units regrouped by lane, so each lane runs its own f0 and norm
+  // (the side lanes' then overlap lane 0's first Gram)
+  {
+    std::vector<F0Tile> tiles;
+    tiles.reserve(p.f0tiles.size());
+    p.norm_units.clear();
+    for (int ln = 0; ln < p.n_lanes; ++ln) {
+      p.f0_lane[ln] = (int32_t)tiles.size();
+      p.norm_lane[ln] = (int32_t)p.norm_units.size();
+      for (size_t gi = 0; gi < p.groups.size(); ++gi) {
+        if (p.group_lane[gi] != ln) continue;
+        for (int32_t k = 0; k < p.groups[gi].n; ++k) {
+          const int32_t ui = p.groups[gi].unit_base + k;
+          MuonUnit &u = p.munits[ui];
+          const int32_t b = (int32_t)tiles.size();
+          tiles.insert(tiles.end(), p.f0tiles.begin() + u.tile_begin, p.f0tiles.begin() + u.tile_end);
+          u.tile_begin = b;
+          u.tile_end = (int32_t)tiles.size();
+          p.norm_units.push_back(ui);
+        }
+      }
+    }
+    for (int ln = p.n_lanes; ln <= kMaxLanes; ++ln) {
+      p.f0_lane[ln] = (int32_t)tiles.size();
+      p.norm_lane[ln] = (int32_t)p.norm_units.size();
+    }
+    p.f0tiles.swap(tiles);
+  }
   // per-lane, per-stage tile tables: symmetric Gram/poly take tm <= tn; longest K first
   for (size_t gi = 0; gi < p.groups.size(); ++gi) {
     const Group &g = p.groups[gi];
@@ -454,7 +482,8 @@ size_t table_bytes(const std::vector<T> &v) { return round_up((int64_t)(v.size()
 int upload(sshdp_plan &p) {
   const size_t total = table_bytes(p.munits) + table_bytes(p.f0tiles) + table_bytes(p.aseg_all) +
                        table_bytes(p.aseg_unfused) + table_bytes(p.qregions) + table_bytes(p.qchunks) +
-                       table_bytes(p.q32tiles) + table_bytes(p.cchunks) + table_bytes(p.ns_groups) + 256;
+                       table_bytes(p.q32tiles) + table_bytes(p.cchunks) + table_bytes(p.ns_groups) +
+                       table_bytes(p.norm_units) + 256;
   size_t tiles_total = 0;
   for (auto &ln : p.ns_tiles)
     for (auto &st : ln)
@@ -479,6 +508,7 @@ int upload(sshdp_plan &p) {
   put(p.q32tiles, p.d.q32tiles);
   put(p.cchunks, p.d.cchunks);
   put(p.ns_groups, p.d.ns_groups);
+  put(p.norm_units, p.d.norm_units);
   for (int ln = 0; ln < kMaxLanes; ++ln)
     for (int st = 0; st < 3; ++st)
       for (int sz = 0; sz < 2; ++sz) put(p.ns_tiles[ln][st][sz], p.d.ns_tiles[ln][st][sz]);
