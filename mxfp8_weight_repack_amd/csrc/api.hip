@@ -56,8 +56,11 @@ struct Prof {
   }
 };
 
+// side_adam: the step's unfused AdamW units, run on the last side stream after its
+// Newton-Schulz work (AdamW and Muon units are disjoint; G waits for the join), so they
+// leave the caller's stream; with one stream they are the caller's to launch.
 int run_muon(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_muon_hp *hp, void *ws, size_t ws_bytes,
-             hipStream_t s) {
+             hipStream_t s, const sshdp_adamw_hp *side_adam = nullptr, int64_t step = 0, bool *adam_done = nullptr) {
   if (p->munits.empty()) return SSHDP_OK;
   if (!b->w_main || !b->grad || !b->mom) return SSHDP_ERR_ARG;
   if (!aligned16(b->w_main) || !aligned16(b->grad) || !aligned16(b->mom)) return SSHDP_ERR_ALIGN;
@@ -105,6 +108,13 @@ int run_muon(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_muon_hp *h
         if (e != hipSuccess) return SSHDP_ERR_HIP;
       }
     }
+  }
+  if (p->n_lanes > 1 && side_adam && !p->aseg_unfused.empty()) {
+    hipStream_t ls = p->lane_stream[p->n_lanes - 1];
+    Prof pr(p, 5, ls);
+    if (launch_adamw(p->d.aseg_unfused, (int64_t)p->aseg_unfused.size(), *b, *side_adam, step, ls) != hipSuccess)
+      return SSHDP_ERR_HIP;
+    if (adam_done) *adam_done = true;
   }
   if (p->n_lanes > 1) {
     for (int ln = 1; ln < p->n_lanes; ++ln) {
@@ -237,11 +247,12 @@ int sshdp_update_step(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_m
     if (!b->w_main || !b->w_bf16) return SSHDP_ERR_ARG;
     if (!aligned16(b->w_main) || !aligned16(b->w_bf16)) return SSHDP_ERR_ALIGN;
   }
+  bool adam_done = false;
   if (!p->munits.empty()) {
-    st = run_muon(p, b, mh, ws, ws_bytes, s);
+    st = run_muon(p, b, mh, ws, ws_bytes, s, ah, step, &adam_done);
     if (st != SSHDP_OK) return st;
   }
-  if (!p->aseg_unfused.empty()) {
+  if (!p->aseg_unfused.empty() && !adam_done) {
     Prof pr(p, 5, s);
     st = hip_status(launch_adamw(p->d.aseg_unfused, (int64_t)p->aseg_unfused.size(), *b, *ah, step, s));
   }
