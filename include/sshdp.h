@@ -303,8 +303,7 @@ int sshdp_rs_accumulate(const void *const *inputs, int32_t n_inputs, int32_t in_
  * (fused with G for MXFP8 regions holding only AdamW units; the other AdamW
  * units may run on a plan-owned side stream beside the Newton-Schulz work, as
  * they share no element with a Muon unit), then G for the remaining MXFP8
- * regions (those whose units all belong to one side stream's groups on that
- * stream, as soon as its work ends) and the BF16 regions.  Equivalent to
+ * regions and the BF16 regions.  Equivalent to
  * sshdp_update_muon; sshdp_update_adamw; sshdp_requant_mxfp8; sshdp_cast_bf16.
  * Every argument the plan's parts need is checked before anything is launched
  * (the errors of those calls); mh may be NULL for a plan without Muon units
