@@ -59,10 +59,8 @@ struct Prof {
 // side_adam: the step's unfused AdamW units, run on the last side stream after its
 // Newton-Schulz work (AdamW and Muon units are disjoint; G waits for the join), so they
 // leave the caller's stream; with one stream they are the caller's to launch.
-// side_g: requantise the regions owned by a side lane (see q_lane) on it after its work.
 int run_muon(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_muon_hp *hp, void *ws, size_t ws_bytes,
-             hipStream_t s, const sshdp_adamw_hp *side_adam = nullptr, int64_t step = 0, bool *adam_done = nullptr,
-             bool side_g = false) {
+             hipStream_t s, const sshdp_adamw_hp *side_adam = nullptr, int64_t step = 0, bool *adam_done = nullptr) {
   if (p->munits.empty()) return SSHDP_OK;
   if (!b->w_main || !b->grad || !b->mom) return SSHDP_ERR_ARG;
   if (!aligned16(b->w_main) || !aligned16(b->grad) || !aligned16(b->mom)) return SSHDP_ERR_ALIGN;
@@ -117,15 +115,6 @@ int run_muon(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_muon_hp *h
     if (launch_adamw(p->d.aseg_unfused, (int64_t)p->aseg_unfused.size(), *b, *side_adam, step, ls) != hipSuccess)
       return SSHDP_ERR_HIP;
     if (adam_done) *adam_done = true;
-  }
-  if (p->n_lanes > 1 && side_g) {
-    for (int ln = 1; ln < p->n_lanes; ++ln) {
-      const int64_t q0 = p->q_lane[ln], nq = p->q_lane[ln + 1] - q0;
-      if (nq <= 0) continue;
-      hipStream_t ls = p->lane_stream[ln];
-      Prof pr(p, 7, ls);
-      if (launch_quant(*p, q0, nq, false, *b, nullptr, step, ls) != hipSuccess) return SSHDP_ERR_HIP;
-    }
   }
   if (p->n_lanes > 1) {
     for (int ln = 1; ln < p->n_lanes; ++ln) {
@@ -259,9 +248,8 @@ int sshdp_update_step(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_m
     if (!aligned16(b->w_main) || !aligned16(b->w_bf16)) return SSHDP_ERR_ALIGN;
   }
   bool adam_done = false;
-  const bool side_g = !p->munits.empty() && p->n_lanes > 1 && p->q32tiles.empty();
   if (!p->munits.empty()) {
-    st = run_muon(p, b, mh, ws, ws_bytes, s, ah, step, &adam_done, side_g);
+    st = run_muon(p, b, mh, ws, ws_bytes, s, ah, step, &adam_done);
     if (st != SSHDP_OK) return st;
   }
   if (!p->aseg_unfused.empty() && !adam_done) {
@@ -274,10 +262,7 @@ int sshdp_update_step(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_m
     st = hip_status(launch_quant(*p, 0, p->n_qchunks_fused, true, *b, ah, step, s));
   }
   if (st != SSHDP_OK) return st;
-  // plain chunks left for the caller's stream: lane 0's, or all of them when the side
-  // lanes did not take theirs
-  const int64_t q_end = side_g ? p->q_lane[1] : (int64_t)p->qchunks.size();
-  const int64_t rest = q_end - p->n_qchunks_fused;
+  const int64_t rest = (int64_t)p->qchunks.size() - p->n_qchunks_fused;
   if (rest > 0) {
     Prof pr(p, 7, s);
     st = hip_status(launch_quant(*p, p->n_qchunks_fused, rest, false, *b, nullptr, step, s));

@@ -148,9 +148,6 @@ struct sshdp_plan {
   std::vector<sshdp::QRegion> qregions;
   std::vector<sshdp::QChunk> qchunks;   // fused-eligible chunks first
   int64_t n_qchunks_fused = 0;
-  // the plain (unfused) chunks follow, grouped by the NS lane whose units are the only
-  // units their region holds (lane 0 for the rest): lane l owns [q_lane[l], q_lane[l+1])
-  int64_t q_lane[sshdp::kMaxLanes + 1] = {};
   std::vector<sshdp::Q32Tile> q32tiles; // BLOCK32X32 layout: all requant work
   std::vector<sshdp::CChunk> cchunks;   // BF16 regions
   size_t ws_uscale = 0, ws_partials = 0, ws_bytes = 0;

@@ -381,7 +381,7 @@ void build_elementwise(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
   }
   std::sort(units.begin(), units.end(), [](const Interval &a, const Interval &b) { return a.start < b.start; });
   std::vector<char> fused_node(n, 0);  // AdamW unit handled inside a fused region
-  std::vector<QChunk> fused, plain[kMaxLanes];
+  std::vector<QChunk> fused, plain;
   for (int32_t i = 0; i < n; ++i) {
     const sshdp_node &nd = nodes[i];
     if (nd.quantize == SSHDP_G_BF16) {
@@ -428,21 +428,7 @@ void build_elementwise(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
       for (size_t k = 1; k < inside.size() && eligible; ++k)   // no two runs share a block
         if ((inside[k].start / 32) <= ((inside[k - 1].start + inside[k - 1].len - 1) / 32)) eligible = false;
     }
-    // a plain region whose units are all Muon units of one side lane (plus, on the last
-    // side lane, AdamW units, which run there too) can be requantised on that lane
-    // right after its NS work; anything else waits for the join (lane 0)
-    int lane = 0;
-    if (!eligible && !inside.empty()) {
-      int l0 = -1;
-      bool one = true;
-      for (const Interval &iv : inside) {
-        const int l = iv.opt == SSHDP_OPT_MUON ? p.group_lane[p.node_group[iv.node]] : p.n_lanes - 1;
-        if (l0 < 0) l0 = l;
-        else if (l != l0) one = false;
-      }
-      if (one && l0 > 0) lane = l0;
-    }
-    std::vector<QChunk> &dst = eligible ? fused : plain[lane];
+    std::vector<QChunk> &dst = eligible ? fused : plain;
     size_t next = 0;
     int64_t pos = a;
     while (pos < a + len) {
@@ -478,11 +464,7 @@ void build_elementwise(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
   }
   p.n_qchunks_fused = (int64_t)fused.size();
   p.qchunks = fused;
-  for (int l = 0; l < kMaxLanes; ++l) {
-    p.q_lane[l] = (int64_t)p.qchunks.size();
-    p.qchunks.insert(p.qchunks.end(), plain[l].begin(), plain[l].end());
-  }
-  p.q_lane[kMaxLanes] = (int64_t)p.qchunks.size();
+  p.qchunks.insert(p.qchunks.end(), plain.begin(), plain.end());
   p.stats.n_quant_regions = (int32_t)p.qregions.size();
   for (const Interval &iv : units) {
     if (iv.opt != SSHDP_OPT_ADAMW) continue;
