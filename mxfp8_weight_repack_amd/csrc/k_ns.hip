@@ -563,7 +563,8 @@ __global__ __launch_bounds__(C::NT, C::NT == 256 ? 2 : 1) void k_ns(NsArgs a) {
   const bool zero = s == 0.f;                       // all-zero momentum: direction is exactly 0
   if (zero && STAGE != 3) return;
   const int64_t rp = g.r_pad, cp = g.c_pad;
-  uint16_t *X = reinterpret_cast<uint16_t *>(a.ws + g.off_x) + tl.b * rp * cp;
+  // X is not stored for groups whose Gram reads X^T (K-major)
+  uint16_t *X = g.km ? nullptr : reinterpret_cast<uint16_t *>(a.ws + g.off_x) + tl.b * rp * cp;
   uint16_t *XT0 = reinterpret_cast<uint16_t *>(a.ws + g.off_xt0) + tl.b * rp * cp;
   uint16_t *XT1 = reinterpret_cast<uint16_t *>(a.ws + g.off_xt1) + tl.b * rp * cp;
   uint16_t *A = reinterpret_cast<uint16_t *>(a.ws + g.off_a) + tl.b * rp * rp;
@@ -595,7 +596,7 @@ __global__ __launch_bounds__(C::NT, C::NT == 256 ? 2 : 1) void k_ns(NsArgs a) {
     if (STAGE == 2) {
       gemm_core<C, true>(reinterpret_cast<const char *>(B + r0 * rp),
                          reinterpret_cast<const char *>(XTc + c0 * rp), rp, smem, acc, r0, a.ca);
-      store_tile<C>(acc, al, 0.f, nullptr, 0, g.km ? nullptr : X, cp, XTn, rp, r0, c0, smem);
+      store_tile<C>(acc, al, 0.f, nullptr, 0, X, cp, XTn, rp, r0, c0, smem);
     } else {
       if (!zero)
         gemm_core<C, true>(reinterpret_cast<const char *>(B + r0 * rp),
