@@ -1,6 +1,6 @@
 """Benchmark: one MI355X's share of the SS-HSDP update phase.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--layout L] [--no-cpu] [--no-graph]
+    python bench.py [--steps K] [--warmup W] [--config 2] [--layout L] [--ns-tiles P] [--g G] [--no-cpu] [--no-graph]
     python bench.py --part rs [--config N]      (the reduce-scatter tail)
 
 A step is one sshdp_update_step over the whole workload: Muon momentum,
@@ -50,6 +50,8 @@ def parse():
                     help="scale layout (default: the workload's own); block32x32 = one scale per 32x32 block")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--ns-tiles", choices=["auto", "small", "large"], default="auto",
+                    help="Newton-Schulz tile policy of the plan (default: the planner's choice)")
     ap.add_argument("--g", choices=["mxfp8", "bf16"], default="mxfp8",
                     help="G on the runtime weights: MXFP8 requant (default) or a bfloat16 cast")
     ap.add_argument("--cpu-budget", type=float, default=25.0, help="seconds of oracle work to aim for")
@@ -234,7 +236,7 @@ def main():
     nodes = wl.nodes
     if args.g == "bf16":                      # every G region becomes a bfloat16 cast
         nodes = [dict(nd, quantize="bf16") if nd["quantize"] else nd for nd in nodes]
-    plan = sh.Plan(nodes, wl.root_numel, layout=layout)
+    plan = sh.Plan(nodes, wl.root_numel, layout=layout, ns_tiles=args.ns_tiles)
     st = plan.stats()
     w = torch.from_numpy(w0).to(dev)
     g = torch.from_numpy(g0).to(dev)
@@ -348,7 +350,8 @@ def main():
         "config": {"workload": wl.name, "params": wl.params, "root_numel": wl.root_numel,
                    "muon_units": st["n_muon_units"], "adamw_units": st["n_adamw_units"],
                    "ns_groups": [[gi["r"], gi["c"], gi["n_units"]] for gi in plan.groups()],
-                   "scale_layout": layout, "g": args.g, "ns_tflop_per_step": st["ns_flops"] / 1e12},
+                   "scale_layout": layout, "g": args.g, "ns_tiles": args.ns_tiles,
+                   "ns_tflop_per_step": st["ns_flops"] / 1e12},
         "roofline": roofline, "repack_roofline": repack, "cast_roofline": cast, "components": components,
         "graph_ms_per_step": graph_ms,
     }
