@@ -14,6 +14,7 @@ namespace sshdp {
 constexpr int kF0Tile = 64;          // f0 transposing tile edge (elements)
 constexpr int kNsSmall = 128;        // Newton-Schulz GEMM macro tiles: 128 x 128 (4 waves) ...
 constexpr int kNsLarge = 256;        // ... or 256 x 256 (8 waves), chosen per group and stage
+constexpr int64_t kNsCacheBytes = 256ll << 20;  // last-level cache (MALL) of the chip
 constexpr int kMaxLanes = 4;         // Newton-Schulz groups run on up to 4 concurrent streams
 constexpr int kChunk = 4096;         // elements per AdamW / requant work item
 constexpr size_t kAlign = 256;       // workspace sub-buffer alignment (bytes)
@@ -136,6 +137,7 @@ struct sshdp_plan {
   // streams joined back by events); per lane, stage and tile size a tile table, longest K first
   int n_lanes = 1;
   std::vector<int32_t> group_lane;
+  bool ns_cached = false;             // NS stage outputs stored cacheable (working set fits the last-level cache)
   // f0 tiles and the units whose norms they feed, contiguous per lane: lane l owns tiles
   // [f0_lane[l], f0_lane[l+1]) and units norm_units[norm_lane[l] .. norm_lane[l+1])
   int32_t f0_lane[sshdp::kMaxLanes + 1] = {};

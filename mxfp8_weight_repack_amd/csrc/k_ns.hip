@@ -379,7 +379,25 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
 // otherwise evict the operand lines that the other tiles of the launch are
 // still streaming through L2.  smem must be free (all fragment reads done) and
 // hold max(TM*(TN+8), TN*(TM+8))*2 bytes.
-template <class C>
+// Copies an R x W bf16 tile from LDS (pitch W+8) to global rows of pitch ld,
+// 16 bytes per lane.  NT: nontemporal stores, for outputs that would only
+// evict operand lines; otherwise ordinary stores, so an output that the next
+// stage reads and that fits the last-level cache stays there.
+template <class C, int R, int W, bool NT>
+__device__ __forceinline__ void copy_out(const uint16_t *lt, uint16_t *dst, int64_t ld) {
+  constexpr int CH = W / 8, P = W + 8;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < R * CH / C::NT; ++k) {
+    const int id = t + C::NT * k, row = id / CH, ch = id - row * CH;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(&lt[row * P + ch * 8]);
+    u32x4_t *q = reinterpret_cast<u32x4_t *>(dst + (int64_t)row * ld + ch * 8);
+    if (NT) __builtin_nontemporal_store(v, q);
+    else *q = v;
+  }
+}
+
+template <class C, bool CACHED = false>
 __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[C::MBM][C::MBN], float alpha, float beta,
                                            const uint16_t *DT, int64_t lddt, uint16_t *O, int64_t ldo, uint16_t *OT,
                                            int64_t ldt, int r0, int c0, char *smem) {
@@ -419,13 +437,7 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[C::MBM][C::MBN]
   }
   if (O) {
     __syncthreads();
-    constexpr int CH = C::TN / 8;                    // 16-byte chunks per row
-#pragma unroll
-    for (int k = 0; k < C::TM * CH / C::NT; ++k) {
-      const int id = t + C::NT * k, row = id / CH, ch = id - row * CH;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(&lt[row * LP + ch * 8]);
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(O + (int64_t)(r0 + row) * ldo + c0 + ch * 8));
-    }
+    copy_out<C, C::TM, C::TN, !CACHED>(lt, O + (int64_t)r0 * ldo + c0, ldo);
   }
   if (!OT) return;
   __syncthreads();
@@ -441,13 +453,7 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[C::MBM][C::MBN]
       }
     }
   __syncthreads();
-  constexpr int CHT = C::TM / 8;
-#pragma unroll
-  for (int k = 0; k < C::TN * CHT / C::NT; ++k) {
-    const int id = t + C::NT * k, col = id / CHT, ch = id - col * CHT;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(&lt[col * LPT + ch * 8]);
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(OT + (int64_t)(c0 + col) * ldt + r0 + ch * 8));
-  }
+  copy_out<C, C::TN, C::TM, !CACHED>(lt, OT + (int64_t)c0 * ldt + r0, ldt);
 }
 
 // f2 on a tile of the last update product: w <- w*decay - lr*scale*x for the
@@ -551,8 +557,10 @@ struct NsArgs {
   int iter;
 };
 
-// STAGE: 0 Gram, 1 poly, 2 update, 3 update + f2
-template <int STAGE, class C>
+// STAGE: 0 Gram, 1 poly, 2 update, 3 update + f2.  CACHED: the stage's outputs
+// are stored with ordinary stores (they and the rest of the step's NS working
+// set fit the last-level cache, so the next stage reads them from there).
+template <int STAGE, class C, bool CACHED>
 __global__ __launch_bounds__(C::NT, C::NT == 256 ? 2 : 1) void k_ns(NsArgs a) {
   constexpr int TILE = C::TM;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
@@ -582,12 +590,12 @@ __global__ __launch_bounds__(C::NT, C::NT == 256 ? 2 : 1) void k_ns(NsArgs a) {
                    smem, acc);
     }
     const float al = a.iter == 0 ? s * s : 1.f;
-    store_tile<C>(acc, al, 0.f, nullptr, 0, A, rp, tl.tm != tl.tn ? A : nullptr, rp, r0, c0, smem);
+    store_tile<C, CACHED>(acc, al, 0.f, nullptr, 0, A, rp, tl.tm != tl.tn ? A : nullptr, rp, r0, c0, smem);
   } else if (STAGE == 1) {
     // B = c (A A + (b/c) A); the A term is Q^T = A[c0.., r0..]^T, taken from LDS
     gemm_core<C, true>(reinterpret_cast<const char *>(A + r0 * rp), reinterpret_cast<const char *>(A + c0 * rp),
                        rp, smem, acc, r0, a.cb / a.cc);
-    store_tile<C>(acc, a.cc, 0.f, nullptr, 0, B, rp, tl.tm != tl.tn ? B : nullptr, rp, r0, c0, smem);
+    store_tile<C, CACHED>(acc, a.cc, 0.f, nullptr, 0, B, rp, tl.tm != tl.tn ? B : nullptr, rp, r0, c0, smem);
   } else {
     const uint16_t *XTc = (a.iter & 1) ? XT1 : XT0;
     uint16_t *XTn = (a.iter & 1) ? XT0 : XT1;
@@ -596,7 +604,7 @@ __global__ __launch_bounds__(C::NT, C::NT == 256 ? 2 : 1) void k_ns(NsArgs a) {
     if (STAGE == 2) {
       gemm_core<C, true>(reinterpret_cast<const char *>(B + r0 * rp),
                          reinterpret_cast<const char *>(XTc + c0 * rp), rp, smem, acc, r0, a.ca);
-      store_tile<C>(acc, al, 0.f, nullptr, 0, X, cp, XTn, rp, r0, c0, smem);
+      store_tile<C, CACHED>(acc, al, 0.f, nullptr, 0, X, cp, XTn, rp, r0, c0, smem);
     } else {
       if (!zero)
         gemm_core<C, true>(reinterpret_cast<const char *>(B + r0 * rp),
@@ -651,8 +659,12 @@ using CSmall = Cfg<kNsSmall, kNsSmall, 2, 2>;   // 4 waves, two workgroups per C
 using CLarge = Cfg<kNsLarge, kNsLarge, 2, 4>;   // 8 waves (two per SIMD), one workgroup per CU
 
 template <int STAGE, class C>
-hipError_t launch_list(const NsArgs &a, size_t n, hipStream_t s) {
-  hipLaunchKernelGGL((k_ns<STAGE, C>), dim3((unsigned)n), dim3(C::NT), 0, s, a);
+hipError_t launch_list(const NsArgs &a, size_t n, bool cached, hipStream_t s) {
+  // the last update stores no stage output: one instantiation
+  if (cached && STAGE != 3)
+    hipLaunchKernelGGL((k_ns<STAGE, C, STAGE != 3>), dim3((unsigned)n), dim3(C::NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_ns<STAGE, C, false>), dim3((unsigned)n), dim3(C::NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -661,12 +673,12 @@ hipError_t launch_sizes(const sshdp_plan &p, NsArgs a, int ln, int st, hipStream
   hipError_t e = hipSuccess;
   if (!p.ns_tiles[ln][st][1].empty()) {       // 256-tile work first: it is the long part
     a.tiles = p.d.ns_tiles[ln][st][1];
-    e = launch_list<STAGE, CLarge>(a, p.ns_tiles[ln][st][1].size(), s);
+    e = launch_list<STAGE, CLarge>(a, p.ns_tiles[ln][st][1].size(), p.ns_cached, s);
     if (e != hipSuccess) return e;
   }
   if (!p.ns_tiles[ln][st][0].empty()) {
     a.tiles = p.d.ns_tiles[ln][st][0];
-    e = launch_list<STAGE, CSmall>(a, p.ns_tiles[ln][st][0].size(), s);
+    e = launch_list<STAGE, CSmall>(a, p.ns_tiles[ln][st][0].size(), p.ns_cached, s);
   }
   return e;
 }

@@ -319,6 +319,13 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
     }
     p.f0tiles.swap(tiles);
   }
+  // Stage outputs that the next stage reads back (X, X^T, A, B) are stored cacheable when the
+  // NS working set of all groups, which run concurrently on the lanes, fits the last-level
+  // cache; otherwise they would only evict operand lines and are stored nontemporal.
+  int64_t ns_set = 0;
+  for (const Group &g : p.groups)
+    ns_set += (int64_t)g.n * g.r_pad * (g.c_pad + 2 * g.r_pad) * 2;
+  p.ns_cached = ns_set <= kNsCacheBytes;
   // per-lane, per-stage tile tables: symmetric Gram/poly take tm <= tn; longest K first
   for (size_t gi = 0; gi < p.groups.size(); ++gi) {
     const Group &g = p.groups[gi];
