@@ -42,7 +42,7 @@
 // each stage reloaded as soon as the barrier ending its step has passed;
 // 128-byte LDS rows whose 16-byte chunks are XOR-swizzled so fragment reads
 // are bank-conflict free; fragment reads and buffer loads are interleaved one
-// per MFMA.  Epilogue through LDS (bf16 pack in hardware), nontemporal stores.
+// per MFMA.  Epilogue through LDS (bf16 pack in hardware), 16-byte stores.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -366,19 +366,6 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
   }
 }
 
-// Epilogue of a TM x TN product: x = alpha*acc + beta*D, rounded to bf16,
-// stored row-major to O (leading dim ldo; skipped if O is null) and, if OT,
-// transposed to OT[col*ldt + row].
-// D is read through its transpose DT (DT[col*lddt + row] = D[row][col]): element
-// (m, n) of a 32x32 MFMA block sits in lane n + 32*((m/4)%2), register
-// (m/8)*4 + m%4, so a lane holds 4 consecutive rows of one column and the D^T
-// read is 8 contiguous bytes.  Both stores go through LDS so that every lane
-// writes 16 contiguous bytes and a wave writes whole rows: first the tile
-// row-major (2-byte LDS writes), then, for O^T, column-major (8-byte LDS writes
-// of the lane's 4 rows).  The global stores are nontemporal: they would
-// otherwise evict the operand lines that the other tiles of the launch are
-// still streaming through L2.  smem must be free (all fragment reads done) and
-// hold max(TM*(TN+8), TN*(TM+8))*2 bytes.
 // Copies an R x W bf16 tile from LDS (pitch W+8) to global rows of pitch ld,
 // 16 bytes per lane.  NT: nontemporal stores, for outputs that would only
 // evict operand lines; otherwise ordinary stores, so an output that the next
@@ -397,6 +384,20 @@ __device__ __forceinline__ void copy_out(const uint16_t *lt, uint16_t *dst, int6
   }
 }
 
+// Epilogue of a TM x TN product: x = alpha*acc + beta*D, rounded to bf16,
+// stored row-major to O (leading dim ldo; skipped if O is null) and, if OT,
+// transposed to OT[col*ldt + row].
+// D is read through its transpose DT (DT[col*lddt + row] = D[row][col]): element
+// (m, n) of a 32x32 MFMA block sits in lane n + 32*((m/4)%2), register
+// (m/8)*4 + m%4, so a lane holds 4 consecutive rows of one column and the D^T
+// read is 8 contiguous bytes.  Both stores go through LDS so that every lane
+// writes 16 contiguous bytes and a wave writes whole rows: first the tile
+// row-major (2-byte LDS writes), then, for O^T, column-major (8-byte LDS writes
+// of the lane's 4 rows).  The global stores are nontemporal unless CACHED:
+// ordinary stores would evict the operand lines that the other tiles of the
+// launch are still streaming, which only pays off when the outputs fit the
+// last-level cache and the next stage reads them there.  smem must be free
+// (all fragment reads done) and hold max(TM*(TN+8), TN*(TM+8))*2 bytes.
 template <class C, bool CACHED = false>
 __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[C::MBM][C::MBN], float alpha, float beta,
                                            const uint16_t *DT, int64_t lddt, uint16_t *O, int64_t ldo, uint16_t *OT,
