@@ -297,8 +297,14 @@ def rs_accumulate(inputs, in_dtype, g, n, first, stream=None):
                                      int(bool(first)), _stream(stream)), "sshdp_rs_accumulate")
 
 
+def _ref(x):
+    """Pointer to a ctypes structure, or NULL for None."""
+    return None if x is None else ctypes.byref(x)
+
+
 def update_step(plan, bufs, mhp, ahp, step, workspace, workspace_bytes, stream=None):
-    _check(lib().sshdp_update_step(plan.handle, ctypes.byref(bufs), ctypes.byref(mhp), ctypes.byref(ahp),
+    """mhp (ahp) may be None for a plan without Muon (AdamW) units."""
+    _check(lib().sshdp_update_step(plan.handle, ctypes.byref(bufs), _ref(mhp), _ref(ahp),
                                    int(step), _ptr(workspace), int(workspace_bytes), _stream(stream)),
            "sshdp_update_step")
 

@@ -258,6 +258,7 @@ int sshdp_update_step(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_m
   }
   if (st != SSHDP_OK) return st;
   if (p->n_qchunks_fused > 0) {
+    if (!ah) return SSHDP_ERR_ARG;                 // fused chunks exist only beside AdamW units
     Prof pr(p, 6, s);
     st = hip_status(launch_quant(*p, 0, p->n_qchunks_fused, true, *b, ah, step, s));
   }

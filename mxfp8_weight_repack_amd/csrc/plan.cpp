@@ -424,6 +424,8 @@ void build_elementwise(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
       if (it->opt != SSHDP_OPT_ADAMW) eligible = false;
       if (it->start < a || it->start + it->len > a + len) eligible = false;
     }
+    // a region holding no unit has no AdamW to fuse: plain G chunks
+    if (inside.empty()) eligible = false;
     // every AdamW unit touching the region must lie entirely inside it
     if (eligible) {
       for (const Interval &iv : inside) {

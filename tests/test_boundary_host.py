@@ -144,6 +144,19 @@ def test_planner_groups_and_stats_on_workloads():
     assert e.value.name == "SCHEMA"
 
 
+def test_planner_fuses_g_only_beside_adamw_units():
+    """A quantised region is fused into the AdamW pass only when AdamW units lie
+    in it; a region holding no unit gets plain G."""
+    st = _plan(workloads.degenerate("g_only").nodes, workloads.degenerate("g_only").root_numel, "rowmajor").stats()
+    assert st["n_quant_regions"] == 2 and st["quant_elems"] == 64 * 256 + 3 * 96 and st["fused_quant_elems"] == 0
+    wl = workloads.degenerate("adamw_g")
+    st = _plan(wl.nodes, wl.root_numel, "rowmajor").stats()
+    assert st["n_adamw_units"] == 1 and st["quant_elems"] == 4 * 224 + 32 * 128 and st["fused_quant_elems"] == 4 * 224
+    wl = workloads.degenerate("muon_only")
+    st = _plan(wl.nodes, wl.root_numel, "rowmajor").stats()
+    assert st["n_muon_units"] == 2 and st["n_adamw_units"] == 0 and st["quant_elems"] == 0
+
+
 def test_planner_argument_errors():
     wl = workloads.config(1)
     with pytest.raises(sh.SshdpError) as e:

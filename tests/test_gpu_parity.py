@@ -224,6 +224,37 @@ def test_update_step_parity(case):
     say(f"  worst NS rel-Frobenius {worst:.3e}")
 
 
+@pytest.mark.parametrize("kind", ["g_only", "muon_only", "adamw_g"])
+def test_update_step_degenerate_plans(kind):
+    """A plan without Muon units, without AdamW units or without anything to
+    quantise: the step takes NULL for the hyper-parameters and buffers of the
+    missing part (as the ABI allows) and still matches the oracle; a quantised
+    region holding no unit gets plain G (not the fused AdamW pass)."""
+    wl = workloads.degenerate(kind)
+    say(f"update_step {wl.name}")
+    S = DeviceState(wl)
+    n = S.stats
+    muon, adam, quant = n["n_muon_units"] > 0, n["n_adamw_units"] > 0, n["n_quant_regions"] > 0
+    if kind == "g_only" or kind == "adamw_g":
+        assert n["fused_quant_elems"] == (0 if kind == "g_only" else 4 * 224)
+    b = sh.buffers(S.w, S.g if muon or adam else None, S.m if muon or adam else None, S.v if adam else None,
+                   S.codes if quant else None, S.scales if quant else None)
+    if quant:
+        with pytest.raises(sh.SshdpError) as e:                # G needs its code and scale roots
+            sh.update_step(S.plan, sh.buffers(S.w, S.g, S.m, S.v), sh.muon_hp(**MUON), sh.adamw_hp(**ADAM), 1,
+                           S.ws, S.ws_bytes, S.stream())
+        assert e.value.name == "ARG"
+    sh.update_step(S.plan, b, sh.muon_hp(**MUON) if muon else None, sh.adamw_hp(**ADAM) if adam else None, 1,
+                   S.ws if muon else None, S.ws_bytes if muon else 0, S.stream())
+    h = S.host()
+    w0, g = wl.arrays()
+    z = np.zeros_like(w0)
+    ref, dirs = oracle_step(wl, wl.scale_layout, w0, g, z, z, 1)
+    check_step(wl, wl.scale_layout, h, ref, dirs, w0)
+    if quant:
+        assert np.any(h["codes"] != 0)
+
+
 @pytest.mark.parametrize("policy", ["small", "large", "auto"])
 def test_update_step_parity_tile_policies(policy):
     """Newton-Schulz products split into a 256-tile leading block and 128-tile

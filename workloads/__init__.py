@@ -219,6 +219,27 @@ def random_units(cid=102, n=6, name="random Muon shapes"):
     return _finish(cid, name, t, "rowmajor")
 
 
+def degenerate(kind):
+    """Plans with a whole optimizer or G missing.  "g_only": quantised regions
+    that hold no unit (G alone); "muon_only": Muon units, nothing quantised, no
+    AdamW; "adamw_g": an AdamW unit inside a quantised region (G fused into the
+    AdamW pass) beside a quantised region with no unit (plain G)."""
+    t = _Tree()
+    if kind == "g_only":
+        t.region(64, 256, quant=True)
+        t.region(3, 96, quant=True)
+        return _finish(110, "G only (quantised regions, no units)", t, "rowmajor")
+    if kind == "muon_only":
+        t.region(48, 160, unit=True, opt="muon")
+        t.region(201, 72, unit=True, opt="muon")
+        return _finish(111, "Muon only (no AdamW, nothing quantised)", t, "rowmajor")
+    if kind == "adamw_g":
+        t.region(4, 224, unit=True, opt="adamw", quant=True)
+        t.region(32, 128, quant=True)
+        return _finish(112, "AdamW + G beside a unit-less quantised region", t, "rowmajor")
+    raise ValueError(kind)
+
+
 def _finish(cid, name, t, layout):
     params = 0
     for n in t.nodes:
