@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SSHDP_ABI_VERSION 3
+#define SSHDP_ABI_VERSION 4
 
 /* Status codes.  The planning errors are the rejections of [SS-HSDP Appendix A,
  * Table 4]: incompatible metadata, invalid geometry, storage overlap. */
@@ -95,11 +95,14 @@ enum { SSHDP_SCALE_ROWMAJOR = 0, SSHDP_SCALE_TILE32X4 = 1, SSHDP_SCALE_BLOCK32X3
  * within the Newton-Schulz tolerance either way, not bit-identical): by default
  * a group's products run in 256 x 256 tiles over their largest 256-aligned
  * leading block when the group is large enough to fill the GPU with them, and
- * in 128 x 128 tiles elsewhere.  Setting both tile flags is an argument error. */
+ * in 128 x 128 tiles elsewhere.  Setting both tile flags is an argument error.
+ * Gram products that run in 128-tiles read X^T (so only X^T is stored) unless
+ * SSHDP_PLAN_NS_GRAM_NT is set or X^T of the unit exceeds 2^31 bytes. */
 enum {
   SSHDP_PLAN_HOST_ONLY = 1,       /* plan and validate on the host; no device tables (cannot launch) */
   SSHDP_PLAN_NS_TILES_SMALL = 2,  /* every Newton-Schulz product in 128 x 128 tiles                  */
-  SSHDP_PLAN_NS_TILES_LARGE = 4   /* 256 x 256 tiles over every 256-aligned leading block            */
+  SSHDP_PLAN_NS_TILES_LARGE = 4,  /* 256 x 256 tiles over every 256-aligned leading block            */
+  SSHDP_PLAN_NS_GRAM_NT = 8       /* every Gram reads X row-major (X and X^T stored); for comparison */
 };
 
 /* One data-tree node [SS-HSDP §3.2]: a 2-D view (rows x cols, cols contiguous,
@@ -114,7 +117,8 @@ enum {
  *   rows, cols >= 1, offset >= 0, row_stride >= cols if rows > 1   (SCHEMA)
  *   the view lies inside its parent's extent and the root           (BOUNDS)
  *   a Muon unit is 2-D (rows, cols >= 2) and its first element, row_stride
- *     and cols are multiples of 4 (16-byte vectors)                (SCHEMA)
+ *     and cols are multiples of 4 (16-byte vectors); rows, cols <= 4194176
+ *     (a 256-row bf16 panel of that length spans < 2^31 bytes)     (SCHEMA)
  *   quantize is SSHDP_G_NONE, SSHDP_G_MXFP8 or SSHDP_G_BF16          (SCHEMA)
  *   an MXFP8 region is contiguous (row_stride == cols), with cols and its
  *     first element multiples of 32; for TILE32X4 also rows % 32 == 0 and
@@ -209,7 +213,7 @@ typedef struct {
                               /* the rest in 128-tiles (0: all 128)                          */
   int32_t upd256_rows;        /* update rows [0, upd256_rows) x columns [0, upd256_cols)    */
   int32_t upd256_cols;        /* run in 256-tiles, the rest in 128-tiles                     */
-  int32_t pad_;
+  int32_t gram_kmajor;        /* 1: the Gram reads X^T (K-major) and X itself is not stored  */
 } sshdp_group_info;
 
 /* Fill *opts with the defaults above. */
@@ -319,7 +323,11 @@ int sshdp_update_step(const sshdp_plan *plan, const sshdp_buffers *bufs, const s
  * update product reads X), or NULL (beta ignored); OT (optional) receives
  * O[b]^T (N x M).  M, N must be multiples of `tile` (128 or 256), K of 64.
  * tile 1281 / 2561: the same 128 / 256 tiles with both operands K-major (the
- * Gram read from X^T): P[b] K x M, Q[b] K x N row-major, M == N, D NULL. */
+ * Gram read from X^T): P[b] K x M, Q[b] K x N row-major, M == N, D NULL.
+ * Errors: ARG (null P, Q or O, non-positive sizes, unknown tile, K-major with D
+ * or M != N), SCHEMA (sizes not multiples of the tile, or an operand panel that
+ * one buffer resource cannot address: tile * K * 2 bytes, K-major
+ * ((K - 1) * M + tile) * 2 bytes, at least 2^31), ALIGN. */
 int sshdp_gemm_bf16_nt(const void *P, const void *Q, const void *D, void *O, void *OT, int32_t M,
                        int32_t N, int32_t K, int32_t batch, float alpha, float beta, int32_t tile,
                        void *stream);

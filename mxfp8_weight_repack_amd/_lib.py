@@ -24,6 +24,9 @@ LAYOUT = {"rowmajor": 0, "tile32x4": 1, "block32x32": 2}
 PLAN_HOST_ONLY = 1
 # Newton-Schulz tile policy: planner default, all 128 x 128, or 256 x 256 over every 256-aligned block
 NS_TILES = {"auto": 0, "small": 2, "large": 4}
+# Gram operand: planner default (128-tile Grams read X^T), or X row-major for every Gram
+NS_GRAM = {"auto": 0, "nt": 8}
+ABI_VERSION = 4                     # SSHDP_ABI_VERSION of the header this binding follows
 PROF_CLASSES = ["momentum", "norm", "ns_gram", "ns_poly", "ns_update", "adamw", "adamw_requant", "requant",
                 "ns_phase", "cast_bf16"]
 # node["quantize"]: False/None (no G), True or "mxfp8" (MXFP8 codes + scales), "bf16" (bfloat16 cast)
@@ -79,7 +82,7 @@ class GroupInfo(ctypes.Structure):
     _fields_ = [("r", ctypes.c_int32), ("c", ctypes.c_int32), ("r_pad", ctypes.c_int32),
                 ("c_pad", ctypes.c_int32), ("n_units", ctypes.c_int32), ("tile", ctypes.c_int32),
                 ("tile_gram", ctypes.c_int32), ("gram256", ctypes.c_int32), ("upd256_rows", ctypes.c_int32),
-                ("upd256_cols", ctypes.c_int32), ("pad_", ctypes.c_int32)]
+                ("upd256_cols", ctypes.c_int32), ("gram_kmajor", ctypes.c_int32)]
 
 
 # every symbol include/sshdp.h declares, with its argument and return types
@@ -127,6 +130,8 @@ def lib():
             f = getattr(L, name)
             f.argtypes = args
             f.restype = res
+        if L.sshdp_abi_version() != ABI_VERSION:
+            raise ImportError(f"{LIB_PATH} has ABI {L.sshdp_abi_version()}, the binding expects {ABI_VERSION}: rebuild it")
         _lib = L
     return _lib
 
@@ -185,14 +190,14 @@ class Plan:
     """A resolved data tree (sshdp_plan_views) and its tables."""
 
     def __init__(self, nodes, root_numel, layout="rowmajor", ns_steps=5, ns_a=3.4445, ns_b=-4.7750, ns_c=2.0315,
-                 ns_eps=1e-7, nesterov=False, scale_mode=0, host_only=False, ns_tiles="auto"):
+                 ns_eps=1e-7, nesterov=False, scale_mode=0, host_only=False, ns_tiles="auto", ns_gram="auto"):
         o = default_opts()
         o.ns_steps, o.ns_a, o.ns_b, o.ns_c, o.ns_eps = ns_steps, ns_a, ns_b, ns_c, ns_eps
         o.scale_layout = LAYOUT[layout]
         o.nesterov = int(bool(nesterov))
         o.muon_scale_mode = scale_mode
         # an unknown policy sets both tile flags, which the library rejects (ARG)
-        o.flags = (PLAN_HOST_ONLY if host_only else 0) | NS_TILES.get(ns_tiles, 6)
+        o.flags = (PLAN_HOST_ONLY if host_only else 0) | NS_TILES.get(ns_tiles, 6) | NS_GRAM.get(ns_gram, 16)
         self._nodes = node_array(nodes)
         self._h = ctypes.c_void_p()
         self.layout = layout

@@ -287,6 +287,9 @@ int sshdp_gemm_bf16_nt(const void *P, const void *Q, const void *D, void *O, voi
   if (tile != 128 && tile != 256 && tile != 1281 && tile != 2561) return SSHDP_ERR_ARG;
   const int tt = tile == 1281 ? 128 : tile == 2561 ? 256 : tile;
   if (M % tt || N % tt || K % 64) return SSHDP_ERR_SCHEMA;
+  // each operand panel is one buffer resource with 32-bit byte offsets
+  const int64_t span = tt == tile ? (int64_t)tt * K * 2 : ((int64_t)K - 1) * M * 2 + (int64_t)tt * 2;
+  if (span > 0x7FFFFFFF) return SSHDP_ERR_SCHEMA;
   if (tt != tile && (D || M != N)) return SSHDP_ERR_ARG;
   if (!aligned16(P) || !aligned16(Q) || (D && !aligned16(D)) || !aligned16(O) || (OT && !aligned16(OT)))
     return SSHDP_ERR_ALIGN;

@@ -14,6 +14,9 @@ namespace sshdp {
 constexpr int kF0Tile = 64;          // f0 transposing tile edge (elements)
 constexpr int kNsSmall = 128;        // Newton-Schulz GEMM macro tiles: 128 x 128 (4 waves) ...
 constexpr int kNsLarge = 256;        // ... or 256 x 256 (8 waves), chosen per group and stage
+// Longest edge of a Muon unit: a 256-row operand panel of K bf16 elements is one
+// buffer resource with 32-bit byte offsets (256 * K * 2 < 2^31), K a multiple of 128
+constexpr int64_t kNsMaxEdge = (int64_t)0x7FFFFFFF / (2 * kNsLarge) / kNsSmall * kNsSmall;
 constexpr int64_t kNsCacheBytes = 256ll << 20;  // last-level cache (MALL) of the chip
 constexpr int kMaxLanes = 4;         // Newton-Schulz groups run on up to 4 concurrent streams
 constexpr int kChunk = 4096;         // elements per AdamW / requant work item

@@ -66,7 +66,7 @@ int validate(const sshdp_node *nodes, int32_t n, int64_t root_numel, int layout,
     if (nd.is_unit && nd.optimizer == SSHDP_OPT_MUON) {
       if (nd.rows < 2 || nd.cols < 2) return SSHDP_ERR_SCHEMA;
       if (a % 4 || rs % 4 || nd.cols % 4) return SSHDP_ERR_SCHEMA;
-      if (nd.rows > (1 << 30) || nd.cols > (1 << 30)) return SSHDP_ERR_SCHEMA;
+      if (nd.rows > kNsMaxEdge || nd.cols > kNsMaxEdge) return SSHDP_ERR_SCHEMA;
     }
     if (nd.quantize != SSHDP_G_NONE && nd.quantize != SSHDP_G_MXFP8 && nd.quantize != SSHDP_G_BF16)
       return SSHDP_ERR_SCHEMA;
@@ -196,7 +196,11 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
       // 4-10% while the single-output epilogue saves ~8% of every update, more where
       // the update's K is short (MoE r = 1408).  256-tile Grams lose ~10% that way and
       // keep the NT form.
-      g.km = g.g256 == 0 ? 1 : 0;
+      // The K-major operand is all of X^T (c_pad x r_pad) behind one buffer resource, so
+      // its byte offsets must stay below 2^31; larger units, and plans asking for it,
+      // read X row-major.
+      const bool km_fits = ((int64_t)g.c_pad - 1) * g.r_pad * 2 + kNsLarge * 2 <= (int64_t)0x7FFFFFFF;
+      g.km = g.g256 == 0 && km_fits && !(p.opts.flags & SSHDP_PLAN_NS_GRAM_NT) ? 1 : 0;
     }
     g.n = (int32_t)kv.second.size();
     g.unit_base = (int32_t)p.munits.size();
@@ -579,7 +583,7 @@ int sshdp_plan_views(const sshdp_node *nodes, int32_t n_nodes, int64_t root_nume
   if (o.ns_steps < 1 || o.ns_steps > 64 || (o.scale_layout != SSHDP_SCALE_ROWMAJOR &&
       o.scale_layout != SSHDP_SCALE_TILE32X4 && o.scale_layout != SSHDP_SCALE_BLOCK32X32) ||
       o.muon_scale_mode < 0 || o.muon_scale_mode > 2 ||
-      !(o.ns_eps >= 0.0f) || (o.flags & ~7u) ||
+      !(o.ns_eps >= 0.0f) || (o.flags & ~15u) ||
       ((o.flags & SSHDP_PLAN_NS_TILES_SMALL) && (o.flags & SSHDP_PLAN_NS_TILES_LARGE)))
     return SSHDP_ERR_ARG;
   std::vector<int64_t> abs, ext;
@@ -621,6 +625,7 @@ int sshdp_plan_group(const sshdp_plan *p, int32_t g, sshdp_group_info *info) {
   info->r = G.r; info->c = G.c; info->r_pad = G.r_pad; info->c_pad = G.c_pad;
   info->n_units = G.n; info->tile = G.u256r ? kNsLarge : kNsSmall; info->tile_gram = G.g256 ? kNsLarge : kNsSmall;
   info->gram256 = G.g256; info->upd256_rows = G.u256r; info->upd256_cols = G.u256c;
+  info->gram_kmajor = G.km;
   return SSHDP_OK;
 }
 

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
         assert name in _lib.SIGNATURES, name
     assert set(_lib.SIGNATURES) == set(decl)
-    assert L.sshdp_abi_version() == 3
+    assert L.sshdp_abi_version() == 4
     assert L.sshdp_status_string(-5) == b"geometry or metadata the kernels cannot take"
 
 
@@ -155,6 +155,55 @@ def test_planner_fuses_g_only_beside_adamw_units():
     wl = workloads.degenerate("muon_only")
     st = _plan(wl.nodes, wl.root_numel, "rowmajor").stats()
     assert st["n_muon_units"] == 2 and st["n_adamw_units"] == 0 and st["quant_elems"] == 0
+
+
+def _one_unit(rows, cols):
+    return [dict(parent=-1, offset=0, rows=rows, cols=cols, row_stride=cols, is_unit=True, optimizer="muon",
+                 quantize=False)]
+
+
+def test_planner_ns_size_limits_and_gram_operand():
+    """A Muon unit's edges stop where a 256-row bf16 operand panel reaches 2^31
+    bytes; a 128-tile Gram reads X^T only while all of X^T (c_pad x r_pad) is
+    addressable with 32-bit byte offsets, else X; ns_gram="nt" reads X always."""
+    edge = 4194176                                   # largest multiple of 128 with 256 * edge * 2 < 2^31
+    assert 256 * edge * 2 < 2 ** 31 <= 256 * (edge + 128) * 2
+    for rows, cols in ((128, edge + 4), (edge + 4, 128)):
+        with pytest.raises(sh.SshdpError) as e:
+            _plan(_one_unit(rows, cols), rows * cols)
+        assert e.value.name == "SCHEMA"
+    assert _plan(_one_unit(128, edge), 128 * edge).group(0)["gram_kmajor"] == 1
+    # X^T of 1024 x 1048576 ends below byte 2^31; of 1024 x 1048704 it does not
+    for cols, km in ((1048576, 1), (1048704, 0)):
+        g = _plan(_one_unit(1024, cols), 1024 * cols).group(0)
+        assert (g["r_pad"], g["c_pad"], g["gram256"], g["gram_kmajor"]) == (1024, cols, 0, km)
+        assert ((cols - 1) * 1024 * 2 + 512 < 2 ** 31) == bool(km)
+    wl = workloads.config(2)
+    assert [g["gram_kmajor"] for g in _plan(wl.nodes, wl.root_numel).groups()] == [1, 1, 1]
+    nt = sh.Plan(wl.nodes, wl.root_numel, host_only=True, ns_gram="nt")
+    assert [g["gram_kmajor"] for g in nt.groups()] == [0, 0, 0]
+    assert nt.stats()["workspace_bytes"] > _plan(wl.nodes, wl.root_numel).stats()["workspace_bytes"]
+    wl = workloads.config(5)
+    assert [(g["gram256"] > 0, g["gram_kmajor"]) for g in _plan(wl.nodes, wl.root_numel).groups()] == \
+        [(False, 1), (True, 0), (True, 0)]
+    with pytest.raises(sh.SshdpError) as e:
+        sh.Plan(wl.nodes, wl.root_numel, host_only=True, ns_gram="bogus")
+    assert e.value.name == "ARG"
+
+
+def test_raw_contraction_size_limits():
+    """The raw contraction refuses operand panels that one buffer resource
+    cannot address, before touching any pointer (the pointers here are fake)."""
+    fake = 1 << 12
+    cases = [(256, 256, 1 << 23, 256), (128, 128, 1 << 24, 128),      # tile * K * 2 = 2^32
+             (2048, 2048, 1 << 20, 1281), (2048, 2048, 1 << 20, 2561)]   # ((K - 1) * M + tile) * 2 > 2^31
+    for M, N, K, tile in cases:
+        # every case must be refused: a case the library accepted would launch on the fake pointers
+        span = tile * K * 2 if tile in (128, 256) else ((K - 1) * M + tile // 10) * 2
+        assert span >= 2 ** 31, (M, N, K, tile)
+        with pytest.raises(sh.SshdpError) as e:
+            sh.gemm_bf16_nt(fake, fake, None, fake, None, M, N, K, 1, 1.0, 0.0, tile)
+        assert e.value.name == "SCHEMA", (M, N, K, tile)
 
 
 def test_planner_argument_errors():

@@ -255,16 +255,22 @@ def test_update_step_degenerate_plans(kind):
         assert np.any(h["codes"] != 0)
 
 
-@pytest.mark.parametrize("policy", ["small", "large", "auto"])
-def test_update_step_parity_tile_policies(policy):
+@pytest.mark.parametrize("policy,gram", [("small", "auto"), ("large", "auto"), ("auto", "auto"),
+                                         ("small", "nt"), ("auto", "nt")])
+def test_update_step_parity_tile_policies(policy, gram):
     """Newton-Schulz products split into a 256-tile leading block and 128-tile
     strips (Gram/poly: the column strip and its mirror; update: the L-shaped
     rest) against the oracle, with every product in 128-tiles, and with the
-    planner's own choice."""
+    planner's own choice; each also with every Gram reading X row-major
+    (gram="nt") instead of X^T."""
     wl = workloads.mixed_tiles()
-    say(f"update_step {wl.name} tiles={policy}")
-    st = DeviceState(wl, plan_kw=dict(ns_tiles=policy))
+    say(f"update_step {wl.name} tiles={policy} gram={gram}")
+    st = DeviceState(wl, plan_kw=dict(ns_tiles=policy, ns_gram=gram))
     groups = st.plan.groups()
+    if gram == "nt":
+        assert all(g["gram_kmajor"] == 0 for g in groups)
+    else:
+        assert all(g["gram_kmajor"] == (g["gram256"] == 0) for g in groups)
     if policy == "large":
         assert any(0 < g["gram256"] < g["r_pad"] for g in groups)
         assert any(0 < g["upd256_rows"] < g["r_pad"] for g in groups)
