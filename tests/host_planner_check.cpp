@@ -45,8 +45,8 @@ int main(int argc, char **argv) {
     for (int g = 0; g < s.n_groups; ++g) {
       sshdp_group_info gi{};
       if (sshdp_plan_group(p, g, &gi) != SSHDP_OK) return 6;
-      std::printf(" [%d %d %d %d %d %d %d %d]", gi.r, gi.c, gi.r_pad, gi.c_pad, gi.n_units, gi.gram256,
-                  gi.upd256_rows, gi.upd256_cols);
+      std::printf(" [%d %d %d %d %d %d %d %d %d]", gi.r, gi.c, gi.r_pad, gi.c_pad, gi.n_units, gi.gram256,
+                  gi.upd256_rows, gi.upd256_cols, gi.gram_kmajor);
     }
     for (int i = 0; i < n; ++i) {
       int64_t a = -1;

@@ -13,7 +13,7 @@ import subprocess
 import pytest
 
 import mxfp8_weight_repack_amd as sh
-from mxfp8_weight_repack_amd._lib import LAYOUT, NS_TILES, node_array
+from mxfp8_weight_repack_amd._lib import LAYOUT, NS_GRAM, NS_TILES, node_array
 import workloads
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -35,6 +35,14 @@ def _trees():
             out.append((wl.nodes, wl.root_numel, "rowmajor", pol))
     wl = workloads.config(2, small=True)
     out.append((wl.nodes, wl.root_numel, "block32x32", "auto"))
+    for pol in ("auto+nt", "small+nt"):                              # every Gram reading X row-major
+        out.append((wl.nodes, wl.root_numel, "tile32x4", pol))
+    for kind in ("g_only", "muon_only", "adamw_g"):
+        wl = workloads.degenerate(kind)
+        out.append((wl.nodes, wl.root_numel, wl.scale_layout, "auto"))
+    big = dict(parent=-1, offset=0, rows=1024, cols=1048704, row_stride=1048704, is_unit=True, optimizer="muon",
+               quantize=False)                                       # X^T past 2^31 bytes: row-major Gram
+    out.append(([big], 1024 * 1048704, "rowmajor", "auto"))
     # rejected trees: overlap, bad parent, out of bounds, misaligned MXFP8 region, bad Muon unit
     base = dict(parent=-1, offset=0, rows=64, cols=64, row_stride=64, is_unit=True, optimizer="muon",
                 quantize=False)
@@ -47,24 +55,28 @@ def _trees():
     ]
     for nodes in bad:
         out.append((nodes, 4096, "rowmajor", "auto"))
+    long = dict(base, rows=128, cols=4194304, row_stride=4194304)       # Muon edge beyond 4194176
+    out.append(([long], 128 * 4194304, "rowmajor", "auto"))
     return out
 
 
 def _write(path, trees):
     with open(path, "wb") as f:
         for nodes, root, layout, pol in trees:
-            f.write(struct.pack("<iqiI", len(nodes), root, LAYOUT[layout], NS_TILES[pol]))
+            tiles, _, gram = pol.partition("+")
+            f.write(struct.pack("<iqiI", len(nodes), root, LAYOUT[layout], NS_TILES[tiles] | NS_GRAM[gram or "auto"]))
             f.write(bytes(node_array(nodes)))
 
 
 def _expected(nodes, root, layout, pol):
+    tiles, _, gram = pol.partition("+")
     try:
-        p = sh.Plan(nodes, root, layout=layout, host_only=True, ns_tiles=pol)
+        p = sh.Plan(nodes, root, layout=layout, host_only=True, ns_tiles=tiles, ns_gram=gram or "auto")
     except sh.SshdpError as e:
         return ("status", e.code)
     st = p.stats()
     groups = [(g["r"], g["c"], g["r_pad"], g["c_pad"], g["n_units"], g["gram256"], g["upd256_rows"],
-               g["upd256_cols"]) for g in p.groups()]
+               g["upd256_cols"], g["gram_kmajor"]) for g in p.groups()]
     return ("ok", st["workspace_bytes"], st["scale_bytes"], st["n_groups"], st["ns_tile_flops"], groups)
 
 
