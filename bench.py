@@ -1,6 +1,7 @@
 """Benchmark: one MI355X's share of the SS-HSDP update phase.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--layout L] [--ns-tiles P] [--g G] [--no-cpu] [--no-graph]
+    python bench.py [--steps K] [--warmup W] [--config 2] [--layout L] [--ns-tiles P] [--ns-gram O] [--g G]
+                    [--no-cpu] [--no-graph]
     python bench.py --part rs [--config N]      (the reduce-scatter tail)
 
 A step is one sshdp_update_step over the whole workload: Muon momentum,
@@ -52,6 +53,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--ns-tiles", choices=["auto", "small", "large"], default="auto",
                     help="Newton-Schulz tile policy of the plan (default: the planner's choice)")
+    ap.add_argument("--ns-gram", choices=["auto", "nt"], default="auto",
+                    help="Gram operand: the planner's choice (X^T for 128-tile Grams) or X row-major everywhere")
     ap.add_argument("--g", choices=["mxfp8", "bf16"], default="mxfp8",
                     help="G on the runtime weights: MXFP8 requant (default) or a bfloat16 cast")
     ap.add_argument("--cpu-budget", type=float, default=25.0, help="seconds of oracle work to aim for")
@@ -236,7 +239,7 @@ def main():
     nodes = wl.nodes
     if args.g == "bf16":                      # every G region becomes a bfloat16 cast
         nodes = [dict(nd, quantize="bf16") if nd["quantize"] else nd for nd in nodes]
-    plan = sh.Plan(nodes, wl.root_numel, layout=layout, ns_tiles=args.ns_tiles)
+    plan = sh.Plan(nodes, wl.root_numel, layout=layout, ns_tiles=args.ns_tiles, ns_gram=args.ns_gram)
     st = plan.stats()
     w = torch.from_numpy(w0).to(dev)
     g = torch.from_numpy(g0).to(dev)
@@ -350,7 +353,7 @@ def main():
         "config": {"workload": wl.name, "params": wl.params, "root_numel": wl.root_numel,
                    "muon_units": st["n_muon_units"], "adamw_units": st["n_adamw_units"],
                    "ns_groups": [[gi["r"], gi["c"], gi["n_units"]] for gi in plan.groups()],
-                   "scale_layout": layout, "g": args.g, "ns_tiles": args.ns_tiles,
+                   "scale_layout": layout, "g": args.g, "ns_tiles": args.ns_tiles, "ns_gram": args.ns_gram,
                    "ns_tflop_per_step": st["ns_flops"] / 1e12},
         "roofline": roofline, "repack_roofline": repack, "cast_roofline": cast, "components": components,
         "graph_ms_per_step": graph_ms,
