@@ -221,7 +221,7 @@ def bench_rs(args, wl):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no "
               f"multi-GPU path: run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
