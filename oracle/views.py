@@ -22,7 +22,12 @@ A node is a mapping with keys
 
 Reading taken where the pages are silent: the planner's error classes and their
 precedence (one rule list, first failing node in index order, overlap last) are
-this implementation's own; the conditions themselves are those of Table 4.
+this implementation's own; the conditions themselves are those of Table 4:
+geometry, bounds, storage overlap, a Muon unit being a matrix, and MXFP8
+regions covering whole 1x32 blocks along their contiguous dimension (the block
+the scale belongs to, OCP-MX) in the chosen scale layout.  Restrictions that
+come from one implementation's memory access (vector widths, alignment of a
+strided view) are not rules of the method and are not checked here.
 """
 
 import numpy as np
@@ -41,12 +46,13 @@ def _extent(rows, cols, row_stride):
     return (rows - 1) * row_stride + cols
 
 
-def resolve_views(nodes, root_numel, scale_layout="rowmajor"):
+def resolve_views(nodes, root_numel, scale_layout="rowmajor", check_overlap=True):
     """Resolve accumulated offsets and validate the tree.
 
     Returns a list of dicts: the input keys plus ``abs`` (absolute element
     offset in the root) and ``extent``.  Raises ViewError on the first
-    violated rule.
+    violated rule; the storage-overlap rule, checked last, is skipped when
+    ``check_overlap`` is false.
     """
     if len(nodes) == 0 or root_numel <= 0:
         raise ViewError("ARG", "empty node table or root")
@@ -72,15 +78,11 @@ def resolve_views(nodes, root_numel, scale_layout="rowmajor"):
             raise ViewError("SCHEMA", f"node {i}: unknown G mode {qv!r}")
         q = qv in (True, "mxfp8", 1)
         cast = qv in ("bf16", 2)
-        if cast and (rs != cols or cols % 8 or a % 8):
-            raise ViewError("SCHEMA", f"node {i}: bf16 region not contiguous or not 8-aligned")
         if is_unit and opt not in ("muon", "adamw"):
             raise ViewError("SCHEMA", f"node {i}: unit without a known optimizer")
         if is_unit and opt == "muon":
             if rows < 2 or cols < 2:
                 raise ViewError("SCHEMA", f"node {i}: Muon unit must be a matrix")
-            if a % 4 or rs % 4 or cols % 4:
-                raise ViewError("SCHEMA", f"node {i}: Muon unit not 16-byte aligned")
         if q:
             if rs != cols or cols % 32 or a % 32:
                 raise ViewError("SCHEMA", f"node {i}: quantised region not block aligned")
@@ -92,6 +94,8 @@ def resolve_views(nodes, root_numel, scale_layout="rowmajor"):
         r.update(abs=a, extent=ext, row_stride=rs, rows=rows, cols=cols,
                  is_unit=is_unit, optimizer=opt if is_unit else None, quantize=q, cast=cast)
         out.append(r)
+    if not check_overlap:
+        return out
     # storage overlap, by brute force marking [SS-HSDP Appendix A, Table 4]
     for key, what in (("is_unit", "units"), ("quantize", "G regions")):
         marks = np.zeros(root_numel, dtype=np.uint8)

@@ -1,7 +1,8 @@
 """The C-ABI library on the host (no GPU): it loads, exports every function
 include/sshdp.h declares, and its planner (run host-only) resolves offsets,
-rejects bad trees with the same error class as the oracle's rule list
-[SS-HSDP Appendix A, Table 4], and groups Muon units by oriented shape
+rejects bad trees with the error class of the oracle's rule list
+[SS-HSDP Appendix A, Table 4] plus the library's own access rules
+(tests/boundary_rules.py), and groups Muon units by oriented shape
 [SS-HSDP §4.1].  No compute call is made."""
 
 import os
@@ -15,6 +16,7 @@ from mxfp8_weight_repack_amd import _lib
 import oracle
 from oracle.views import ViewError
 import workloads
+from boundary_rules import expected_code
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -70,11 +72,9 @@ def test_planner_agrees_with_oracle_rules_on_random_trees(layout):
     root = 16384 if layout == "block32x32" else 2048
     for _ in range(3000):
         nodes = _random_tree(rng, root, blocks32=layout == "block32x32")
-        try:
+        exp = expected_code(nodes, root, layout)
+        if exp is None:
             res = oracle.resolve_views(nodes, root, layout)
-            exp = None
-        except ViewError as e:
-            exp = e.code
         try:
             p = _plan(nodes, root, layout)
             got = None

@@ -175,6 +175,116 @@ def test_adamw_constant_gradient_closed_form():
         assert np.max(np.abs(w - ref)) <= 2e-6 * np.max(np.abs(ref))
 
 
+def _golden_adamw():
+    from fractions import Fraction
+    path = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden", "adamw.txt")
+    rows = []
+    for ln in open(path):
+        f = ln.split("#", 1)[0].split()
+        if f and f[0] == "adamw":
+            rows.append((int(f[1]), float(f[2]), *(Fraction(x) for x in f[3:6])))
+    return rows
+
+
+def test_adamw_hand_worked_three_steps():
+    """Three steps worked by hand with exactly representable hyper-parameters
+    (tests/golden/adamw.txt): m and v exactly, w to float32 rounding."""
+    rows = _golden_adamw()
+    assert [r[0] for r in rows] == [1, 2, 3]
+    hp = dict(lr=0.5, beta1=0.5, beta2=0.75, eps=0.0, weight_decay=0.25)
+    w, m, v = np.float32([1.0]), np.float32([0.0]), np.float32([0.0])
+    for t, g, m_exp, v_exp, w_exp in rows:
+        w, m, v = oracle.adamw_step(w, np.float32([g]), m, v, t, **hp)
+        assert m[0] == float(m_exp) and v[0] == float(v_exp), t
+        assert abs(float(w[0]) - float(w_exp)) <= 2 ** -24 * abs(float(w_exp)), t
+
+
+def _adam_sums(w0, gs, t, lr, b1, b2, eps, wd):
+    """AdamW after t steps in its explicit-sum form: m_t = (1-b1) sum b1^(t-k) g_k,
+    v_t = (1-b2) sum b2^(t-k) g_k^2, and w_t = rho^t w0 - lr sum rho^(t-k)
+    mhat_k / (sqrt(vhat_k) + eps) with rho = 1 - lr wd (every mhat_k, vhat_k
+    from the sums, not from a recurrence)."""
+    lr, b1, b2, eps, wd = (np.float64(np.float32(x)) for x in (lr, b1, b2, eps, wd))
+    rho = 1.0 - lr * wd
+    G = [np.asarray(g, np.float64) for g in gs[:t]]
+    w = rho ** t * np.asarray(w0, np.float64)
+    for k in range(1, t + 1):
+        mk = (1 - b1) * sum(b1 ** (k - j) * G[j - 1] for j in range(1, k + 1))
+        vk = (1 - b2) * sum(b2 ** (k - j) * G[j - 1] ** 2 for j in range(1, k + 1))
+        w = w - lr * rho ** (t - k) * (mk / (1 - b1 ** k)) / (np.sqrt(vk / (1 - b2 ** k)) + eps)
+    m = (1 - b1) * sum(b1 ** (t - j) * G[j - 1] for j in range(1, t + 1))
+    v = (1 - b2) * sum(b2 ** (t - j) * G[j - 1] ** 2 for j in range(1, t + 1))
+    return w, m, v
+
+
+def _adam_variant(w, g, m, v, t, lr, beta1, beta2, eps, weight_decay, swap=False, no_one_minus=False,
+                  abs_not_square=False, decay_after=False):
+    """AdamW with one planted mistake (for checking that the pins catch it)."""
+    lr, b1, b2, ep, wd = (np.float64(np.float32(x)) for x in (lr, beta1, beta2, eps, weight_decay))
+    if swap:
+        b1, b2 = b2, b1
+    w, g, m, v = (np.asarray(x, np.float64) for x in (w, g, m, v))
+    if not decay_after:
+        w = w - lr * wd * w
+    m = b1 * m + (1.0 if no_one_minus else 1.0 - b1) * g
+    v = b2 * v + (1.0 - b2) * (np.abs(g) if abs_not_square else g * g)
+    w = w - lr * (m / (1 - b1 ** t)) / (np.sqrt(v / (1 - b2 ** t)) + ep)
+    if decay_after:
+        w = w - lr * wd * w
+    return w, m, v
+
+
+def _run_varying(step_fn, w0, gs, T):
+    w, m, v = w0, np.zeros_like(w0), np.zeros_like(w0)
+    out = []
+    for t in range(1, T + 1):
+        w, m, v = step_fn(w, gs[t - 1], m, v, t)
+        out.append((np.asarray(w), np.asarray(m), np.asarray(v)))
+    return out
+
+
+def _varying_pin_error(out, w0, gs, hp):
+    """Worst normwise distance of (w, m, v) after each step from the sum forms."""
+    worst = 0.0
+    for t, (w, m, v) in enumerate(out, 1):
+        ws, ms, vs = _adam_sums(w0, gs, t, **hp)
+        for got, ref in ((w, ws), (m, ms), (v, vs)):
+            worst = max(worst, np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+    return worst
+
+
+def test_adamw_varying_gradient_matches_sum_forms():
+    """A fresh gradient every step (magnitudes spread over two decades): the
+    oracle's w, m and v after each of 8 steps equal the explicit-sum forms to
+    float32 storage rounding."""
+    rng = np.random.default_rng(11)
+    w0 = (rng.standard_normal(2048) * 0.02).astype(np.float32)
+    gs = [(rng.standard_normal(2048) * 1e-3 * 10 ** rng.uniform(-1, 1, 2048)).astype(np.float32) for _ in range(8)]
+    hp = dict(lr=1e-3, b1=0.9, b2=0.95, eps=1e-8, wd=0.1)
+    out = _run_varying(lambda w, g, m, v, t: oracle.adamw_step(w, g, m, v, t, **ADAM), w0, gs, 8)
+    assert _varying_pin_error(out, w0, gs, hp) <= 1e-6
+
+
+def test_adamw_varying_gradient_pin_catches_planted_mistakes():
+    """Mistakes a constant gradient cannot see (bias correction cancels them)
+    fail the varying-gradient pin; the correct form passes it."""
+    rng = np.random.default_rng(12)
+    w0 = (rng.standard_normal(1024) * 0.02).astype(np.float32)
+    gs = [(rng.standard_normal(1024) * 1e-3 * 10 ** rng.uniform(-1, 1, 1024)).astype(np.float32) for _ in range(6)]
+    hp = dict(lr=1e-3, b1=0.9, b2=0.95, eps=1e-8, wd=0.1)
+    good = _run_varying(lambda w, g, m, v, t: _adam_variant(w, g, m, v, t, **ADAM), w0, gs, 6)
+    assert _varying_pin_error(good, w0, gs, hp) <= 1e-9
+    g_const = [gs[0]] * 6
+    for bad in (dict(swap=True), dict(no_one_minus=True), dict(abs_not_square=True), dict(decay_after=True)):
+        out = _run_varying(lambda w, g, m, v, t: _adam_variant(w, g, m, v, t, **ADAM, **bad), w0, gs, 6)
+        assert _varying_pin_error(out, w0, gs, hp) > 2e-6, bad     # beyond the pin's 1e-6
+    # the swap passes a constant gradient's w (m-hat = g, v-hat = g^2 whatever the betas) -- which is why
+    # the varying pin exists
+    out = _run_varying(lambda w, g, m, v, t: _adam_variant(w, g, m, v, t, **ADAM, swap=True), w0, g_const, 6)
+    ws, _, _ = _adam_sums(w0, g_const, 6, **hp)
+    assert np.max(np.abs(out[-1][0] - ws)) <= 1e-9 * np.max(np.abs(ws))
+
+
 def test_adamw_zero_grad_decay_and_padding():
     w0 = np.float32([0.5, -0.25, 0.0, 0.0])
     z = np.zeros(4, np.float32)
