@@ -1,28 +1,38 @@
 """Benchmark: one MI355X's share of the SS-HSDP update phase.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--layout L] [--ns-tiles P] [--ns-gram O] [--g G]
-                    [--no-cpu] [--no-graph]
+    python bench.py [--steps K] [--warmup W] [--config 5] [--repack-config 4] [--layout L] [--ns-tiles P]
+                    [--ns-gram O] [--g G] [--no-cpu] [--no-graph]
     python bench.py --part rs [--config N]      (the reduce-scatter tail)
 
 A step is one sshdp_update_step over the whole workload: Muon momentum,
 batched bf16 MFMA Newton-Schulz, main-weight update, AdamW, and the MXFP8
 requantisation of every runtime weight.  Inputs are seeded synthetic roots,
-resident in HBM before timing starts.  The default workload is the dense
-transformer block (d=2048, 16 heads of 128, 4 KV heads, MLP 8192, per-head
-QKV Muon units), the configuration the metric is quoted on.
+resident in HBM before timing starts.  The default workload is the largest
+one a single GPU holds: the d=8192 dense block (64 heads of 128, 8 KV heads,
+MLP 28672; per-head QKV Muon units, 855.6 M parameters, 148.7 TFLOP of
+Newton-Schulz per step).
 
 Prints one JSON line.  `value` = parameters updated per second (padding
 excluded) from HIP events around K steps on the launch stream (`step_ms`:
-median/min/max of the single steps).  `roofline` covers the Newton-Schulz
-phase, the dominant part: executed MFMA flops of its tile schedule per step
-divided by the phase's time (HIP events from the fork on the launch stream to
-the join of the concurrent streams, in a second pass of K steps), against the
-dense bf16 peak; `traffic` is the phase's HBM-side bytes per step from the
-counter runs recorded in profiles/traffic.json (null when the kernel sources
-changed since).  `repack_roofline` is G (with AdamW where fused) against HBM
-bandwidth.  `graph_ms_per_step` is the same step captured once into a HIP
-graph and replayed K times (context only; `value` is the eager figure).
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+median/min/max of the single steps).
+
+`roofline` is the dominant kernel's: the Newton-Schulz update product
+X' = aX + BX of the groups on the launch stream (for the d=8192 block, the
+three 8192 x 28672 MLP units in 256-tiles), its executed MFMA flops per launch
+(zero-momentum units excluded) over its average launch time from HIP events
+bracketing each launch on that stream, against the dense bf16 peak; `traffic`
+is its HBM-side bytes per launch from the FETCH_SIZE / WRITE_SIZE counter runs
+recorded in profiles/traffic.json (null when the kernel sources changed
+since).  `ns_phase` is the whole Newton-Schulz phase (every group, concurrent
+streams) over its wall time.
+
+`repack_roofline` is the other half of the metric, AdamW + MXFP8 repack, timed
+in the same run on the flat ragged shard of 5e8 elements (--repack-config):
+the fused AdamW+G pass at 29.03125 algorithmic bytes per element against HBM
+bandwidth.  `g_roofline` is the main workload's own G.  `graph_ms_per_step` is
+the same step captured once into a HIP graph and replayed K times (context
+only; `value` is the eager figure).  `cpu_baseline` times the CPU oracle on a
+bounded sample of the main workload and extrapolates to one whole step.
 """
 
 import argparse
@@ -46,7 +56,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=5,
+                    help="workload (1-5; default 5, the d=8192 dense block, the largest one GPU holds)")
+    ap.add_argument("--repack-config", type=int, default=4,
+                    help="workload whose fused AdamW + MXFP8 pass gives repack_roofline, timed in the same run "
+                         "(default 4, the flat 5e8-element shard; 0 = none)")
     ap.add_argument("--layout", choices=["rowmajor", "tile32x4", "block32x32"], default=None,
                     help="scale layout (default: the workload's own); block32x32 = one scale per 32x32 block")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -78,9 +92,10 @@ def source_digest(names):
 
 
 def measured_traffic(workload, part):
-    """HBM bytes per step of `part` ("ns_phase" or "repack") on `workload`, from
-    the counter runs recorded in profiles/traffic.json, or None when there are
-    none or the kernel sources changed since they were taken."""
+    """HBM-side bytes per launch of `part` ("dominant": the kernel `roofline`
+    covers; "repack": the fused AdamW + G pass) on `workload`, from the counter
+    runs recorded in profiles/traffic.json, or None when there are none or the
+    kernel sources changed since they were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -89,13 +104,21 @@ def measured_traffic(workload, part):
         return None
     if not rec or rec.get("src_digest") != source_digest(rec.get("sources", [])):
         return None
-    return rec["bytes_per_step"]
+    return rec["bytes_per_launch"]
 
 
 def cpu_baseline(wl, budget_s):
-    """Time the oracle (as it stands) on a bounded sample of the workload's
-    units: units are taken in table order until the estimated cost fills the
-    budget; params/s = sampled params / oracle time."""
+    """The oracle (as it stands) on a bounded sample of the workload, extrapolated
+    to one whole update step.
+
+    Per distinct Muon unit shape, one unit runs the oracle's Muon update in full
+    (momentum, normalisation, Newton-Schulz, weight update) when its five
+    float64 Newton-Schulz steps fit the budget's share; larger units run it with
+    0 and with 1 Newton-Schulz step, and the step count scales the difference
+    (each step is the same three products).  AdamW is timed on up to 4 M
+    elements of its units, G on up to 1 M elements of a quantised region; both
+    scale by element count.  params/s = the workload's parameters / the
+    extrapolated step time."""
     import oracle
     from oracle.views import resolve_views, unit_indices
     try:
@@ -108,35 +131,83 @@ def cpu_baseline(wl, budget_s):
     backend = backend or "unknown BLAS"
     w0, g = wl.arrays()
     res = resolve_views(wl.nodes, wl.root_numel, wl.scale_layout)
-    # cost model for picking the sample: ~0.3 us/element elementwise, ~25 GF/s per BLAS thread for NS
-    pick, est = [], 0.0
-    for i, r in enumerate(res):
-        if not r["is_unit"]:
-            continue
-        n = r["rows"] * r["cols"]
-        cost = 3e-7 * n
-        if r["optimizer"] == "muon":
-            rr, cc = min(r["rows"], r["cols"]), max(r["rows"], r["cols"])
-            cost += 5 * (4 * rr * rr * cc + 2 * rr ** 3) / (25e9 * threads)
-        if est + cost > budget_s and pick:
-            continue
-        pick.append(i)
-        est += cost
-    sub = [dict(wl.nodes[i], parent=-1, offset=res[i]["abs"]) for i in pick]
-    w, m, v = w0.copy(), np.zeros_like(w0), np.zeros_like(w0)
-    codes = np.zeros(wl.root_numel, np.uint8)
-    scales = np.zeros((wl.root_numel + 31) // 32, np.uint8)
-    # quantise the sampled units' own elements (their share of G)
-    for nd in sub:
-        nd["quantize"] = nd["cols"] % 32 == 0 and nd["row_stride"] == nd["cols"] and nd["offset"] % 32 == 0
-    params = sum(nd["rows"] * nd["cols"] for nd in sub)
+    hp = oracle.OracleHyper()
+    # a quick BLAS rate for choosing what runs in full
+    a = np.random.default_rng(0).standard_normal((1024, 1024))
     t0 = time.perf_counter()
-    oracle.update_step(sub, wl.root_numel, w, g, m, v, codes, scales, 1, layout="rowmajor")
-    dt = time.perf_counter() - t0
-    return {"value": params / dt, "unit": "params/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(sub)} of {len(wl.units())} units ({params} params, one full update step "
-                      f"incl. their MXFP8 repack) in {dt:.1f} s; NumPy fp64 on {backend}, {threads} BLAS threads",
-            "seconds": dt}
+    _ = a @ a
+    rate = 2 * 1024 ** 3 / max(time.perf_counter() - t0, 1e-6)
+    shapes = {}
+    for i, r in enumerate(res):
+        if r["is_unit"] and r["optimizer"] == "muon":
+            shapes.setdefault((r["rows"], r["cols"]), []).append(i)
+    total, parts, measured = 0.0, [], 0.0
+    for (rows, cols), units in shapes.items():
+        r = res[units[0]]
+        idx = unit_indices(r)
+        rr, cc = min(rows, cols), max(rows, cols)
+        ns_est = hp.ns_steps * (4 * rr * rr * cc + 2 * rr ** 3) / rate
+        z = np.zeros(idx.shape, np.float32)
+        if ns_est <= budget_s / max(len(shapes), 1):
+            t0 = time.perf_counter()
+            oracle.muon_update_unit(w0[idx], g[idx], z, hp)
+            t_unit = time.perf_counter() - t0
+            measured += t_unit
+            how = "full"
+        else:
+            # the unit's update without Newton-Schulz steps (momentum, normalisation, weight
+            # update), then one step's cost as NS(u, 1 step) - NS(u, 0 steps) on the same u
+            t0 = time.perf_counter()
+            oracle.muon_update_unit(w0[idx], g[idx], z, oracle.OracleHyper(ns_steps=0))
+            t_elem = time.perf_counter() - t0
+            u = oracle.momentum_step(z, g[idx], hp.momentum)[1]
+            t = []
+            for k in (0, 1):
+                t0 = time.perf_counter()
+                oracle.newton_schulz(u, k, hp.a, hp.b, hp.c, hp.ns_eps)
+                t.append(time.perf_counter() - t0)
+            measured += t_elem + sum(t)
+            t_unit = t_elem + hp.ns_steps * max(t[1] - t[0], 0.0)
+            how = "no NS step + one NS step"
+        total += len(units) * t_unit
+        parts.append(f"{len(units)} x {rows}x{cols} ({how}: {t_unit:.2f} s/unit)")
+    adam = [r for r in res if r["is_unit"] and r["optimizer"] == "adamw"]
+    if adam:
+        n_all = sum(r["rows"] * r["cols"] for r in adam)
+        done, t_adam = 0, 0.0
+        for r in adam:
+            if done >= 4_000_000:
+                break
+            idx = unit_indices(r)
+            if idx.size > 4_000_000:
+                idx = idx.ravel()[:4_000_000]
+            z = np.zeros(idx.shape, np.float32)
+            t0 = time.perf_counter()
+            oracle.adamw_step(w0[idx], g[idx], z, z, 1, hp.adam_lr, hp.beta1, hp.beta2, hp.adam_eps, hp.adam_wd)
+            t_adam += time.perf_counter() - t0
+            done += idx.size
+        measured += t_adam
+        total += t_adam * n_all / done
+        parts.append(f"AdamW {n_all} elements (timed on {done})")
+    quant = [r for r in res if r["quantize"]]
+    if quant:
+        n_all = sum(r["rows"] * r["cols"] for r in quant)
+        r = max(quant, key=lambda x: x["rows"] * x["cols"])
+        rows = max(1, min(r["rows"], 1_000_000 // r["cols"]))
+        sub = dict(r, rows=rows, extent=rows * r["cols"])
+        n_s = (rows * r["cols"]) // 32 * 32
+        codes = np.zeros(wl.root_numel, np.uint8)
+        scales = np.zeros((wl.root_numel + 31) // 32 + 1, np.uint8)
+        t0 = time.perf_counter()
+        oracle.requant_root(w0, [sub], "rowmajor", codes, scales)
+        t_q = time.perf_counter() - t0
+        measured += t_q
+        total += t_q * n_all / max(n_s, 1)
+        parts.append(f"G {n_all} elements (timed on {n_s})")
+    return {"value": wl.params / total, "unit": "params/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"extrapolated to one whole step ({total:.1f} s) from {measured:.1f} s of oracle work: "
+                      + "; ".join(parts) + f"; NumPy fp64 on {backend}, {threads} BLAS threads",
+            "seconds": measured}
 
 
 def run_env(torch, wl):
@@ -218,6 +289,48 @@ def bench_rs(args, wl):
     print(json.dumps(out), flush=True)
 
 
+class Setup:
+    """Device roots, plan and workspace of one workload (torch for memory only)."""
+
+    def __init__(self, torch, sh, wl, args, layout=None, g_mode="mxfp8"):
+        dev = "cuda:0"
+        self.wl = wl
+        w0, g0 = wl.arrays()
+        self.layout = layout or wl.scale_layout
+        nodes = wl.nodes
+        if g_mode == "bf16":                      # every G region becomes a bfloat16 cast
+            nodes = [dict(nd, quantize="bf16") if nd["quantize"] else nd for nd in nodes]
+        self.plan = sh.Plan(nodes, wl.root_numel, layout=self.layout, ns_tiles=args.ns_tiles, ns_gram=args.ns_gram)
+        self.st = self.plan.stats()
+        self.w = torch.from_numpy(w0).to(dev)
+        self.g = torch.from_numpy(g0).to(dev)
+        self.m = torch.zeros_like(self.w)
+        self.v = torch.zeros_like(self.w) if self.st["n_adamw_units"] else None
+        self.codes = torch.zeros(wl.root_numel, dtype=torch.uint8, device=dev)
+        self.scales = torch.zeros(self.st["scale_bytes"], dtype=torch.uint8, device=dev)
+        self.ws_bytes = max(int(self.st["workspace_bytes"]), 256)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.w16 = torch.empty(wl.root_numel, dtype=torch.bfloat16, device=dev) if g_mode == "bf16" else None
+        self.bufs = sh.buffers(self.w, self.g, self.m, self.v, self.codes, self.scales, w_bf16=self.w16)
+        self.mhp, self.ahp = sh.muon_hp(), sh.adamw_hp()
+        self.sh = sh
+        self.step_no = 0
+
+    def step(self, sp):
+        self.step_no += 1
+        self.sh.update_step(self.plan, self.bufs, self.mhp, self.ahp, self.step_no, self.ws, self.ws_bytes, sp)
+
+    def profiled(self, torch, sp, steps):
+        """K steps with every kernel class bracketed by HIP events on its stream."""
+        self.plan.profile(True)
+        for _ in range(steps):
+            self.step(sp)
+        torch.cuda.synchronize()
+        prof = self.plan.profile_read()
+        self.plan.profile(False)
+        return prof
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -229,38 +342,19 @@ def main():
     import workloads
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = "cuda:0"
     torch.cuda.set_device(0)
     wl = workloads.config(args.config)
     if args.part == "rs":
         return bench_rs(args, wl)
-    w0, g0 = wl.arrays()
-    layout = args.layout or wl.scale_layout
-    nodes = wl.nodes
-    if args.g == "bf16":                      # every G region becomes a bfloat16 cast
-        nodes = [dict(nd, quantize="bf16") if nd["quantize"] else nd for nd in nodes]
-    plan = sh.Plan(nodes, wl.root_numel, layout=layout, ns_tiles=args.ns_tiles, ns_gram=args.ns_gram)
-    st = plan.stats()
-    w = torch.from_numpy(w0).to(dev)
-    g = torch.from_numpy(g0).to(dev)
-    m = torch.zeros_like(w)
-    v = torch.zeros_like(w) if st["n_adamw_units"] else None
-    codes = torch.zeros(wl.root_numel, dtype=torch.uint8, device=dev)
-    scales = torch.zeros(st["scale_bytes"], dtype=torch.uint8, device=dev)
-    ws_bytes = max(int(st["workspace_bytes"]), 256)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    w16 = torch.empty(wl.root_numel, dtype=torch.bfloat16, device=dev) if args.g == "bf16" else None
-    bufs = sh.buffers(w, g, m, v, codes, scales, w_bf16=w16)
-    mhp, ahp = sh.muon_hp(), sh.adamw_hp()
+    S = Setup(torch, sh, wl, args, layout=args.layout, g_mode=args.g)
+    st, layout = S.st, S.layout
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
-    step = 0
     for _ in range(args.warmup):
-        step += 1
-        sh.update_step(plan, bufs, mhp, ahp, step, ws, ws_bytes, sp)
+        S.step(sp)
     if args.copy_probe:
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
@@ -269,8 +363,7 @@ def main():
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     ev[0].record(stream)
     for k in range(args.steps):
-        step += 1
-        sh.update_step(plan, bufs, mhp, ahp, step, ws, ws_bytes, sp)
+        S.step(sp)
         ev[k + 1].record(stream)
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[-1]) / args.steps
@@ -285,7 +378,7 @@ def main():
         gstream.wait_stream(stream)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=gstream):
-            sh.update_step(plan, bufs, mhp, ahp, step + 1, ws, ws_bytes, gstream.cuda_stream)
+            S.sh.update_step(S.plan, S.bufs, S.mhp, S.ahp, S.step_no + 1, S.ws, S.ws_bytes, gstream.cuda_stream)
         torch.cuda.synchronize()
         for _ in range(args.warmup):
             graph.replay()
@@ -296,48 +389,85 @@ def main():
         gev[1].record()
         torch.cuda.synchronize()
         graph_ms = gev[0].elapsed_time(gev[1]) / args.steps
-        step += 1 + args.warmup + args.steps
+        S.step_no += 1 + args.warmup + args.steps
         del graph
 
     # per-kernel-class durations: HIP events bracketing every launch, same K steps
-    plan.profile(True)
-    for _ in range(args.steps):
-        step += 1
-        sh.update_step(plan, bufs, mhp, ahp, step, ws, ws_bytes, sp)
-    torch.cuda.synchronize()
-    prof = plan.profile_read()
-    plan.profile(False)
+    prof = S.profiled(torch, sp, args.steps)
     components = {c: {"ms_per_step": prof[c][0] / args.steps, "launches_per_step": prof[c][1] / args.steps}
                   for c in prof if prof[c][1]}
-    # Newton-Schulz: all groups' contraction launches (concurrent streams) over the NS phase,
-    # fork to join on the launch stream; executed = the MFMA work of the tile schedule
-    roofline = None
-    ns_ms = prof["ns_phase"][0] / args.steps if prof["ns_phase"][1] else 0.0
-    if ns_ms > 0:
-        ns_s = ns_ms / 1e3
-        achieved = st["ns_tile_flops"] / ns_s / 1e12
-        ns_launches = sum(prof[c][1] for c in ("ns_gram", "ns_poly", "ns_update")) / args.steps
-        roofline = {"bound": "mfma",
-                    "kernel": "k_ns (Newton-Schulz contraction: every group's launches, NS phase wall time)",
-                    "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                    "traffic": measured_traffic(wl.name, "ns_phase"),
-                    "executed_tflop_per_step": st["ns_tile_flops"] / 1e12,
-                    "dense_tflop_per_step": st["ns_flops"] / 1e12,
-                    "effective_dense_tflops": st["ns_flops"] / ns_s / 1e12,
-                    "ns_phase_ms": ns_ms, "launches_per_step": ns_launches}
-    # repack (G) HBM fraction: algorithmic bytes 4 (read w) + 1 (code) + 1/32 (scale) per element,
+    groups = S.plan.groups()
+    roofline = ns_phase = None
+    if st["n_muon_units"]:
+        units_nz, exec_flops = S.plan.ns_executed(S.ws, S.ws_bytes, sp)
+        # the dominant kernel: the update product of the groups on the launch stream (steps before the
+        # last); executed MFMA flops per launch = 2 r_pad^2 c_pad per non-zero unit (twice that where B is
+        # held as a bf16 pair)
+        lane0 = [i for i, gi in enumerate(groups) if gi["lane"] == 0]
+        upd_flops = sum(units_nz[i] * 2.0 * groups[i]["r_pad"] ** 2 * groups[i]["c_pad"] *
+                        (2 if groups[i]["split_b"] else 1) for i in lane0)
+        ms_upd, n_upd = prof["lane0_update"]
+        if n_upd and upd_flops > 0:
+            ms_launch = ms_upd / n_upd
+            achieved = upd_flops / (ms_launch / 1e3) / 1e12
+            names = ", ".join(f"{groups[i]['r']}x{groups[i]['c']} x{groups[i]['n_units']}" for i in lane0)
+            tiles = "256-tiles" if all(groups[i]["tile"] == 256 and groups[i]["upd256_rows"] == groups[i]["r_pad"]
+                                       and groups[i]["upd256_cols"] == groups[i]["c_pad"] for i in lane0) \
+                else "256- and 128-tiles"
+            roofline = {"bound": "mfma",
+                        "kernel": f"k_ns update X' = aX + BX ({tiles}; groups {names}; launch stream)",
+                        "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                        "traffic": measured_traffic(wl.name, "dominant"),
+                        "tflop_per_launch": upd_flops / 1e12, "ms_per_launch": ms_launch,
+                        "launches_per_step": n_upd / args.steps,
+                        "timing": "HIP events bracketing each launch on its stream, profiled pass of K steps"}
+        ns_ms = prof["ns_phase"][0] / args.steps if prof["ns_phase"][1] else 0.0
+        if ns_ms > 0:
+            ns_s = ns_ms / 1e3
+            dense = sum(units_nz[i] * 5 * (4.0 * gi["r"] ** 2 * gi["c"] + 2.0 * gi["r"] ** 3)
+                        for i, gi in enumerate(groups))
+            ns_phase = {"bound": "mfma", "achieved": exec_flops / ns_s / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": exec_flops / ns_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                        "executed_tflop_per_step": exec_flops / 1e12,
+                        "dense_tflop_per_step": dense / 1e12,
+                        "effective_dense_tflops": dense / ns_s / 1e12, "ms": ns_ms,
+                        "nonzero_units": int(sum(units_nz)), "units": st["n_muon_units"]}
+    # G (and fused AdamW + G) against HBM: 4 (read w) + 1 (code) + 1/32 (scale) bytes per element,
     # plus 28 B/element of AdamW where it is fused
-    rq_ms = prof["requant"][0] + prof["adamw_requant"][0]
+    per_scale = 1.0 / 1024 if layout == "block32x32" else 1.0 / 32
+
+    def hbm_obj(prof_, st_, steps, kernel):
+        rq_ms = prof_["requant"][0] + prof_["adamw_requant"][0]
+        if rq_ms <= 0:
+            return None
+        fused = st_["fused_quant_elems"]
+        byts = (st_["quant_elems"] - fused) * (5.0 + per_scale) + fused * (29.0 + per_scale)
+        gbs = byts * steps / (rq_ms / 1e3) / 1e9
+        return {"bound": "hbm", "kernel": kernel, "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS, "bytes_per_step": byts, "ms_per_launch": rq_ms / steps}
+
+    g_roof = hbm_obj(prof, st, args.steps, "k_quant (G on the main workload)")
     repack = None
-    if rq_ms > 0:
-        fused = st["fused_quant_elems"]
-        per_scale = 1.0 / 1024 if layout == "block32x32" else 1.0 / 32
-        byts = (st["quant_elems"] - fused) * (5.0 + per_scale) + fused * (29.0 + per_scale)
-        gbs = byts * args.steps / (rq_ms / 1e3) / 1e9
-        repack = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": gbs / HBM_PEAK_GBS, "bytes_per_step": byts,
-                  "traffic": measured_traffic(wl.name, "repack")}
+    repack_wl = None
+    if args.config == args.repack_config:
+        repack = hbm_obj(prof, st, args.steps, "k_quant<true> (AdamW + MXFP8 G fused)")
+        repack_wl = wl
+    elif args.repack_config:
+        # the AdamW + MXFP8 half of the metric, on its own workload, in the same run
+        del S
+        torch.cuda.empty_cache()
+        repack_wl = workloads.config(args.repack_config)
+        R = Setup(torch, sh, repack_wl, argparse.Namespace(ns_tiles="auto", ns_gram="auto"))
+        for _ in range(args.warmup):
+            R.step(sp)
+        torch.cuda.synchronize()
+        rprof = R.profiled(torch, sp, args.steps)
+        repack = hbm_obj(rprof, R.st, args.steps, "k_quant<true> (AdamW + MXFP8 G fused)")
+        del R
+    if repack is not None:
+        repack["workload"] = repack_wl.name
+        repack["traffic"] = measured_traffic(repack_wl.name, "repack")
     cast = None
     if prof["cast_bf16"][0] > 0:          # G as a bfloat16 cast: 4 (read w) + 2 (write) bytes per element
         byts = 6.0 * st["cast_elems"]
@@ -352,11 +482,12 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "params": wl.params, "root_numel": wl.root_numel,
                    "muon_units": st["n_muon_units"], "adamw_units": st["n_adamw_units"],
-                   "ns_groups": [[gi["r"], gi["c"], gi["n_units"]] for gi in plan.groups()],
+                   "ns_groups": [[gi["r"], gi["c"], gi["n_units"]] for gi in groups],
                    "scale_layout": layout, "g": args.g, "ns_tiles": args.ns_tiles, "ns_gram": args.ns_gram,
-                   "ns_tflop_per_step": st["ns_flops"] / 1e12},
-        "roofline": roofline, "repack_roofline": repack, "cast_roofline": cast, "components": components,
-        "graph_ms_per_step": graph_ms,
+                   "ns_tflop_per_step": st["ns_flops"] / 1e12,
+                   "repack_workload": repack_wl.name if repack_wl is not None else None},
+        "roofline": roofline, "ns_phase": ns_phase, "repack_roofline": repack, "g_roofline": g_roof,
+        "cast_roofline": cast, "components": components, "graph_ms_per_step": graph_ms,
     }
     out["env"] = run_env(torch, wl)
     if not args.no_cpu:

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SSHDP_ABI_VERSION 4
+#define SSHDP_ABI_VERSION 5
 
 /* Status codes.  The planning errors are the rejections of [SS-HSDP Appendix A,
  * Table 4]: incompatible metadata, invalid geometry, storage overlap. */
@@ -214,6 +214,10 @@ typedef struct {
   int32_t upd256_rows;        /* update rows [0, upd256_rows) x columns [0, upd256_cols)    */
   int32_t upd256_cols;        /* run in 256-tiles, the rest in 128-tiles                     */
   int32_t gram_kmajor;        /* 1: the Gram reads X^T (K-major) and X itself is not stored  */
+  int32_t split_b;            /* 1 (groups with r_pad == 128): the polynomial B goes to memory  */
+                              /* as a bf16 pair, its rounding and the remainder, and the update */
+                              /* contracts over both (twice the update's K)                     */
+  int32_t lane;               /* stream the group runs on: 0 = the caller's, 1.. = side streams */
 } sshdp_group_info;
 
 /* Fill *opts with the defaults above. */
@@ -248,7 +252,12 @@ int sshdp_update_muon(const sshdp_plan *plan, const sshdp_buffers *bufs, const s
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /* F for every AdamW unit at step `step` (>= 1, caller-owned, same for all
- * units).  Reads grad, mom, adam_v, w_main; writes mom, adam_v, w_main.
+ * units) [SS-HSDP §5.2: the parameters Muon does not take -- 1-D and
+ * elementwise ones -- are updated by AdamW; Appendix B.1: AdamW is the
+ * optimizer of every performance run].  The pages write no AdamW formula; the
+ * form is the sshdp_adamw_hp one above (decay lr*wd on the pre-update weight,
+ * bias-corrected moments, eps after the square root), elementwise in fp32.
+ * Reads grad, mom, adam_v, w_main; writes mom, adam_v, w_main.
  * Errors: ARG (null pointers, step < 1, wrong device), STATE, ALIGN; HIP. */
 int sshdp_update_adamw(const sshdp_plan *plan, const sshdp_buffers *bufs, const sshdp_adamw_hp *hp,
                        int64_t step, void *stream);
@@ -332,6 +341,19 @@ int sshdp_gemm_bf16_nt(const void *P, const void *Q, const void *D, void *O, voi
                        int32_t N, int32_t K, int32_t batch, float alpha, float beta, int32_t tile,
                        void *stream);
 
+/* Diagnostics.  What the Newton-Schulz tile schedule executed in the last
+ * sshdp_update_muon / sshdp_update_step that used `workspace`: a unit whose
+ * momentum was all zero has direction 0 and skips every product, so only the
+ * other units count.  `units_per_group` (n_groups entries, or NULL) receives
+ * each group's count of such units; `flops` (or NULL) the MFMA flops their
+ * tiles executed in that step (stats.ns_tile_flops split per unit, summed over
+ * them).  Reads the per-unit normalisation scales the call left in the
+ * workspace: enqueues a copy on `stream` and synchronises with it.  Errors: ARG
+ * (null plan, wrong device), STATE, WORKSPACE (null or smaller than
+ * stats.workspace_bytes); HIP. */
+int sshdp_ns_executed(const sshdp_plan *plan, const void *workspace, size_t workspace_bytes,
+                      int32_t *units_per_group, double *flops, void *stream);
+
 /* Per-stage kernel timing for benchmarking: when enabled on a plan, launching
  * calls bracket each kernel class with HIP events on the launch stream and
  * accumulate durations (milliseconds) and launch counts; reading synchronises
@@ -339,8 +361,11 @@ int sshdp_gemm_bf16_nt(const void *P, const void *Q, const void *D, void *O, voi
  * 4 NS update (+f2), 5 AdamW, 6 AdamW+G fused, 7 G requant, 8 the whole
  * Newton-Schulz phase on the caller's stream (fork to join: NS launches of
  * different groups run concurrently on plan-owned streams, so classes 2-4 can
- * overlap in time), 9 G bf16 cast.  Not thread-safe; for measurement only. */
-enum { SSHDP_PROF_CLASSES = 10 };
+ * overlap in time), 9 G bf16 cast, and the Newton-Schulz launches of the
+ * caller's stream alone (the groups whose sshdp_group_info.lane is 0): 10 Gram,
+ * 11 poly, 12 update of the steps before the last, 13 the last update (+f2).
+ * Not thread-safe; for measurement only. */
+enum { SSHDP_PROF_CLASSES = 14 };
 int sshdp_profile_enable(sshdp_plan *plan, int32_t enable);
 int sshdp_profile_read(sshdp_plan *plan, double *ms, int64_t *launches);
 

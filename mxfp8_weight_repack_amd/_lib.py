@@ -26,9 +26,9 @@ PLAN_HOST_ONLY = 1
 NS_TILES = {"auto": 0, "small": 2, "large": 4}
 # Gram operand: planner default (128-tile Grams read X^T), or X row-major for every Gram
 NS_GRAM = {"auto": 0, "nt": 8}
-ABI_VERSION = 4                     # SSHDP_ABI_VERSION of the header this binding follows
+ABI_VERSION = 5                     # SSHDP_ABI_VERSION of the header this binding follows
 PROF_CLASSES = ["momentum", "norm", "ns_gram", "ns_poly", "ns_update", "adamw", "adamw_requant", "requant",
-                "ns_phase", "cast_bf16"]
+                "ns_phase", "cast_bf16", "lane0_gram", "lane0_poly", "lane0_update", "lane0_update_last"]
 # node["quantize"]: False/None (no G), True or "mxfp8" (MXFP8 codes + scales), "bf16" (bfloat16 cast)
 GMODE = {None: 0, False: 0, True: 1, "mxfp8": 1, "bf16": 2}
 
@@ -82,7 +82,8 @@ class GroupInfo(ctypes.Structure):
     _fields_ = [("r", ctypes.c_int32), ("c", ctypes.c_int32), ("r_pad", ctypes.c_int32),
                 ("c_pad", ctypes.c_int32), ("n_units", ctypes.c_int32), ("tile", ctypes.c_int32),
                 ("tile_gram", ctypes.c_int32), ("gram256", ctypes.c_int32), ("upd256_rows", ctypes.c_int32),
-                ("upd256_cols", ctypes.c_int32), ("gram_kmajor", ctypes.c_int32)]
+                ("upd256_cols", ctypes.c_int32), ("gram_kmajor", ctypes.c_int32),
+                ("split_b", ctypes.c_int32), ("lane", ctypes.c_int32)]
 
 
 # every symbol include/sshdp.h declares, with its argument and return types
@@ -112,6 +113,8 @@ SIGNATURES = {
                            ctypes.c_int64, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "sshdp_gemm_bf16_nt": ([_P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                             ctypes.c_float, ctypes.c_float, ctypes.c_int32, _P], ctypes.c_int),
+    "sshdp_ns_executed": ([_P, _P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double),
+                           _P], ctypes.c_int),
     "sshdp_profile_enable": ([_P, ctypes.c_int32], ctypes.c_int),
     "sshdp_profile_read": ([_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
 }
@@ -228,6 +231,17 @@ class Plan:
         g = ctypes.c_int32()
         _check(lib().sshdp_plan_node(self.handle, i, ctypes.byref(a), ctypes.byref(g)), "sshdp_plan_node")
         return a.value, g.value
+
+    def ns_executed(self, workspace, workspace_bytes, stream=None):
+        """(units per group, MFMA flops) the Newton-Schulz tiles executed in the
+        last Muon call that used this workspace (units with all-zero momentum
+        count 0); synchronises."""
+        ng = self.stats()["n_groups"]
+        units = (ctypes.c_int32 * max(ng, 1))()
+        f = ctypes.c_double()
+        _check(lib().sshdp_ns_executed(self.handle, _ptr(workspace), int(workspace_bytes), units, ctypes.byref(f),
+                                       _stream(stream)), "sshdp_ns_executed")
+        return [units[i] for i in range(ng)], f.value
 
     def profile(self, enable=True):
         _check(lib().sshdp_profile_enable(self.handle, int(enable)), "sshdp_profile_enable")

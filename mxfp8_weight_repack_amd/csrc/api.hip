@@ -1,12 +1,16 @@
 // api.hip -- the launching entry points of libsshdp.so.
 //
-// [SS-HSDP §3.4 "Update"]: after the microbatches each unit's F runs (Muon:
-// f0 local momentum, f1 Newton-Schulz on the whole unit, f2 local weight
-// update), AdamW runs for the remaining units, and applying G to the updated
-// main weights begins the next cycle.  [SS-HSDP Appendix A]: stages run in
-// order within an update group, each consuming the committed outputs of the
-// previous; here that order is the order of launches on one stream.
-#include <hip/hip_runtime.h>
+// [SS-HSDP §3.4 "Update"]: once the microbatches are done, every unit runs
+// its F (for Muon: f0 on local momentum, f1 Newton-Schulz over the whole
+// unit, f2 on the local weight), the remaining units take AdamW, and G then
+// turns the new main weights into the next iteration's runtime weights.
+// [SS-HSDP Appendix A]: within an update group the stages are ordered, each
+// reading what the previous one committed; here that order is the order of
+// launches on one stream.
+//
+// This file launches no kernel itself (the launchers live beside their
+// kernels), so it needs only the runtime API.
+#include <hip/hip_runtime_api.h>
 
 #include "internal.h"
 
@@ -34,13 +38,13 @@ struct Prof {
   hipStream_t s;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   Prof(const sshdp_plan *pl, int c, hipStream_t st) : p(const_cast<sshdp_plan *>(pl)), cls(c), s(st) {
-    if (!p->prof) return;
+    if (!p->prof || cls < 0) return;
     e0 = take();
     e1 = take();
     if (e0) (void)hipEventRecord(e0, s);
   }
   ~Prof() {
-    if (!p->prof || !e0 || !e1) return;
+    if (!p->prof || cls < 0 || !e0 || !e1) return;
     (void)hipEventRecord(e1, s);
     p->prof_pending.push_back({cls, {e0, e1}});
   }
@@ -54,6 +58,37 @@ struct Prof {
     if (hipEventCreate(&e) != hipSuccess) return nullptr;
     return e;
   }
+};
+
+// The plan's side streams (lanes 1..) forked from the caller's stream by an event.
+// Every lane that has started waiting on the fork is joined back into the caller's
+// stream -- explicitly on success, by the destructor on an error return -- so a call
+// that fails part-way still leaves no side-stream work unordered after the caller's
+// later work (and a capture that began on the caller's stream stays closed).
+struct LaneFork {
+  const sshdp_plan *p;
+  hipStream_t s;
+  int forked = 1;        // lanes [1, forked) wait on the fork
+  LaneFork(const sshdp_plan *pl, hipStream_t st) : p(pl), s(st) {}
+  hipError_t fork() {
+    hipError_t e = hipEventRecord(p->ev_fork, s);
+    for (int ln = 1; e == hipSuccess && ln < p->n_lanes; ++ln) {
+      e = hipStreamWaitEvent(p->lane_stream[ln], p->ev_fork, 0);
+      if (e == hipSuccess) forked = ln + 1;
+    }
+    return e;
+  }
+  hipError_t join() {
+    hipError_t first = hipSuccess;
+    for (int ln = 1; ln < forked; ++ln) {
+      hipError_t e = hipEventRecord(p->ev_join[ln], p->lane_stream[ln]);
+      if (e == hipSuccess) e = hipStreamWaitEvent(s, p->ev_join[ln], 0);
+      if (e != hipSuccess && first == hipSuccess) first = e;
+    }
+    forked = 1;
+    return first;
+  }
+  ~LaneFork() { (void)join(); }
 };
 
 // side_adam: the step's unfused AdamW units, run on the last side stream after its
@@ -83,11 +118,11 @@ int run_muon(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_muon_hp *h
   // Newton-Schulz: lane 0 on the caller's stream, the other lanes on plan-owned
   // streams forked from and joined back into it by events
   Prof wall(p, 8, s);
+  LaneFork lanes(p, s);
   if (p->n_lanes > 1) {
-    if (hipEventRecord(p->ev_fork, s) != hipSuccess) return SSHDP_ERR_HIP;
+    if (lanes.fork() != hipSuccess) return SSHDP_ERR_HIP;
     for (int ln = 1; ln < p->n_lanes; ++ln) {
       hipStream_t ls = p->lane_stream[ln];
-      if (hipStreamWaitEvent(ls, p->ev_fork, 0) != hipSuccess) return SSHDP_ERR_HIP;
       {
         Prof pr(p, 0, ls);
         e = launch_f0(*p, ln, b->grad, b->mom, hp->momentum, p->opts.nesterov, w, ls);
@@ -104,6 +139,7 @@ int run_muon(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_muon_hp *h
       for (int ln = 0; ln < p->n_lanes; ++ln) {
         hipStream_t ls = ln == 0 ? s : p->lane_stream[ln];
         Prof pr(p, 2 + stage, ls);
+        Prof pr0(p, ln == 0 ? 10 + kind : -1, ls);       // the caller's stream's launches alone
         e = launch_ns_stage(*p, ln, kind, it, w, b->w_main, hp->lr, hp->weight_decay, ls);
         if (e != hipSuccess) return SSHDP_ERR_HIP;
       }
@@ -116,13 +152,7 @@ int run_muon(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_muon_hp *h
       return SSHDP_ERR_HIP;
     if (adam_done) *adam_done = true;
   }
-  if (p->n_lanes > 1) {
-    for (int ln = 1; ln < p->n_lanes; ++ln) {
-      if (hipEventRecord(p->ev_join[ln], p->lane_stream[ln]) != hipSuccess) return SSHDP_ERR_HIP;
-      if (hipStreamWaitEvent(s, p->ev_join[ln], 0) != hipSuccess) return SSHDP_ERR_HIP;
-    }
-  }
-  return SSHDP_OK;
+  return lanes.join() == hipSuccess ? SSHDP_OK : SSHDP_ERR_HIP;
 }
 
 int check_adam(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_adamw_hp *hp, int64_t step) {
@@ -295,6 +325,31 @@ int sshdp_gemm_bf16_nt(const void *P, const void *Q, const void *D, void *O, voi
     return SSHDP_ERR_ALIGN;
   return hip_status(launch_gemm_raw(P, Q, D, O, OT, M, N, K, batch, alpha, D ? beta : 0.f, tile,
                                     static_cast<hipStream_t>(stream)));
+}
+
+int sshdp_ns_executed(const sshdp_plan *p, const void *ws, size_t ws_bytes, int32_t *units_per_group,
+                      double *flops, void *stream) {
+  int st = check_plan(p);
+  if (st != SSHDP_OK) return st;
+  if (flops) *flops = 0.0;
+  for (size_t g = 0; units_per_group && g < p->groups.size(); ++g) units_per_group[g] = 0;
+  if (p->munits.empty()) return SSHDP_OK;
+  if (!ws || ws_bytes < p->ws_bytes) return SSHDP_ERR_WORKSPACE;
+  std::vector<float> s(p->munits.size());
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(s.data(), static_cast<const char *>(ws) + p->ws_uscale, s.size() * sizeof(float),
+                     hipMemcpyDeviceToHost, hs) != hipSuccess)
+    return SSHDP_ERR_HIP;
+  if (hipStreamSynchronize(hs) != hipSuccess) return SSHDP_ERR_HIP;
+  double f = 0.0;
+  for (size_t u = 0; u < s.size(); ++u) {
+    if (s[u] == 0.0f) continue;
+    const int g = p->munits[u].group;
+    f += p->group_unit_flops[g];
+    if (units_per_group) units_per_group[g] += 1;
+  }
+  if (flops) *flops = f;
+  return SSHDP_OK;
 }
 
 int sshdp_profile_enable(sshdp_plan *p, int32_t enable) {

@@ -53,6 +53,8 @@ struct Group {
   // Gram/poly rows and columns [0, g256), update rows [0, u256r) x columns [0, u256c)
   int32_t g256, u256r, u256c;
   int32_t km;           // Gram from X^T with transposing LDS reads (128-tile Gram groups)
+  int32_t split;        // r_pad == 128: B kept as a bf16 pair [B_hi | B_lo] (r_pad x 2 r_pad) and the
+                        // update contracts over both halves (K = 2 r_pad, X^T read twice)
   int32_t unit_base;    // first MuonUnit of the group in the device table
   size_t off_x, off_xt0, off_xt1, off_a, off_b;   // workspace byte offsets
 };
@@ -62,7 +64,7 @@ struct NsGroupDev {
   int64_t off_x, off_xt0, off_xt1, off_a, off_b;   // workspace byte offsets
   int32_t r_pad, c_pad, unit_base, n;
   int32_t km;           // Gram read from X^T (K-major); X itself is never stored
-  int32_t pad_;
+  int32_t split;        // B stored as [B_hi | B_lo], row pitch 2 r_pad (see Group::split)
 };
 
 // One macro tile of one stage: group, unit within the group, tile row/column.
@@ -135,6 +137,7 @@ struct sshdp_plan {
   std::vector<sshdp::MuonUnit> munits;
   std::vector<sshdp::F0Tile> f0tiles;
   std::vector<sshdp::Group> groups;
+  std::vector<double> group_unit_flops;   // MFMA flops the tile schedule executes per unit and step
   std::vector<sshdp::NsGroupDev> ns_groups;
   // Newton-Schulz groups are dealt to lanes (lane 0 = the caller's stream, others = plan-owned
   // streams joined back by events); per lane, stage and tile size a tile table, longest K first

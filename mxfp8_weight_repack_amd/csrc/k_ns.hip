@@ -130,11 +130,16 @@ __device__ __forceinline__ int km_swz(int k) { return (k & 3) << 2; }
 // KM: both operands K-major (P stored [K][...] with row pitch ld elements, gP at
 // element (k = 0, first row of the tile), likewise Q): the Gram read from X^T.
 // Fragments come from ds_read_b64_tr_b16 pairs (each gives a lane 4 k of its row).
-template <class C, bool CAPD = false, bool KM = false>
+// SPLITQ: Q has row pitch kq = K/2 and is contracted twice: Q's element k is
+// Q[n][k mod kq] (P = [P_hi | P_lo] against [Q | Q], the update with B held as a
+// bf16 pair).
+template <class C, bool CAPD = false, bool KM = false, bool SPLITQ = false>
 __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_t K, char *smem,
                                           f32x16_t (&acc)[C::MBM][C::MBN], int dk0 = 0, float dscale = 0.f,
                                           int64_t ld = 0) {
   static_assert(!(CAPD && KM), "the added term is read from an NT stage");
+  static_assert(!(SPLITQ && KM), "the split contraction is NT");
+  const int64_t kq = SPLITQ ? K / 2 : K;             // Q's row pitch and K period
   static_assert(!KM || (C::BK == 64 && C::TM % 32 == 0 && C::TN % 32 == 0), "K-major stages: 64 k-rows");
   constexpr int MBM = C::MBM, MBN = C::MBN, NW = C::NW, BK = C::BK, RB = C::RB, CPR = C::CPR, RPI = C::RPI;
   constexpr int NST = C::NST;
@@ -150,10 +155,11 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
   const int drow = RPI * wave + lane / CPR;
   const int dchunk = (lane % CPR) ^ swz<BK>(drow);   // rows drow + RPI*NW*i share the swizzle
   const int voff = (drow * (int)K + dchunk * 8) * 2;
+  const int voffq = SPLITQ ? (drow * (int)kq + dchunk * 8) * 2 : voff;
   const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char *>(gP), 0, KM ? (int)(((K - 1) * ld + C::TM) * 2) : (int)(C::TM * K * 2), kBufWord3);
   const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char *>(gQ), 0, KM ? (int)(((K - 1) * ld + C::TN) * 2) : (int)(C::TN * K * 2), kBufWord3);
+      const_cast<char *>(gQ), 0, KM ? (int)(((K - 1) * ld + C::TN) * 2) : (int)(C::TN * kq * 2), kBufWord3);
   // K-major DMA: a load fills RK = 1024 / (2 T) whole rows (k) of T columns; load i
   // of wave w fills rows RK*(NW*i + w) ..; the row's swizzle depends on k % 4 only
   constexpr int CKA = C::TM / 8, CKB = C::TN / 8;                  // 16-byte chunks per K-major row
@@ -190,6 +196,7 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
   };
   auto dma_q = [&](int stage, int k0) __attribute__((always_inline)) {
     char *sa = smem + stage * C::STAGE + C::SEGA + wave * 1024;
+    if (SPLITQ && k0 >= kq) k0 -= (int)kq;           // the second pass over Q
 #pragma unroll
     for (int i = 0; i < C::NIB; ++i) {
       if (KM)
@@ -197,7 +204,7 @@ __device__ __forceinline__ void gemm_core(const char *gP, const char *gQ, int64_
                                                  16, voffb, (int)((k0 + i * RKB * NW) * ld * 2), 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (__attribute__((address_space(3))) void *)(sa + i * NW * 1024),
-                                                 16, voff, (i * RPI * NW * (int)K + k0) * 2, 0, 0);
+                                                 16, voffq, (i * RPI * NW * (int)kq + k0) * 2, 0, 0);
     }
   };
   bf16x8_t fa0[MBM], fb0[MBN], fa1[MBM], fb1[MBN];
@@ -398,10 +405,12 @@ __device__ __forceinline__ void copy_out(const uint16_t *lt, uint16_t *dst, int6
 // launch are still streaming, which only pays off when the outputs fit the
 // last-level cache and the next stage reads them there.  smem must be free
 // (all fragment reads done) and hold max(TM*(TN+8), TN*(TM+8))*2 bytes.
+// OL (optional, no D): the remainder x - bf16(x), rounded to bf16, stored like O
+// with the same leading dimension (a bf16 pair holding x to ~16 bits).
 template <class C, bool CACHED = false>
 __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[C::MBM][C::MBN], float alpha, float beta,
                                            const uint16_t *DT, int64_t lddt, uint16_t *O, int64_t ldo, uint16_t *OT,
-                                           int64_t ldt, int r0, int c0, char *smem) {
+                                           int64_t ldt, int r0, int c0, char *smem, uint16_t *OL = nullptr) {
   constexpr int LP = C::TN + 8, LPT = C::TM + 8;
   static_assert(C::TM * LP * 2 <= C::LDS && C::TN * LPT * 2 <= C::LDS, "epilogue tile fits LDS");
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave / C::WN, wn = wave % C::WN;
@@ -439,6 +448,32 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[C::MBM][C::MBN]
   if (O) {
     __syncthreads();
     copy_out<C, C::TM, C::TN, !CACHED>(lt, O + (int64_t)r0 * ldo + c0, ldo);
+  }
+  if (OL) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < C::MBM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::MBN; ++j) {
+        const int lc = wn * C::WTN + j * 32 + (lane & 31);
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int lr0 = wm * C::WTM + i * 32 + g4 * 8 + (lane >> 5) * 4;
+          const uint2 h = hp[i][j][g4];
+          const float hi[4] = {__uint_as_float(h.x << 16), __uint_as_float(h.x & 0xFFFF0000u),
+                               __uint_as_float(h.y << 16), __uint_as_float(h.y & 0xFFFF0000u)};
+          float lo[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) lo[q] = alpha * acc[i][j][g4 * 4 + q] - hi[q];
+          const uint32_t l01 = pk_bf16(lo[0], lo[1]), l23 = pk_bf16(lo[2], lo[3]);
+          lt[(lr0 + 0) * LP + lc] = (uint16_t)l01;
+          lt[(lr0 + 1) * LP + lc] = (uint16_t)(l01 >> 16);
+          lt[(lr0 + 2) * LP + lc] = (uint16_t)l23;
+          lt[(lr0 + 3) * LP + lc] = (uint16_t)(l23 >> 16);
+        }
+      }
+    __syncthreads();
+    copy_out<C, C::TM, C::TN, !CACHED>(lt, OL + (int64_t)r0 * ldo + c0, ldo);
   }
   if (!OT) return;
   __syncthreads();
@@ -577,7 +612,10 @@ __global__ __launch_bounds__(C::NT, C::NT == 256 ? 2 : 1) void k_ns(NsArgs a) {
   uint16_t *XT0 = reinterpret_cast<uint16_t *>(a.ws + g.off_xt0) + tl.b * rp * cp;
   uint16_t *XT1 = reinterpret_cast<uint16_t *>(a.ws + g.off_xt1) + tl.b * rp * cp;
   uint16_t *A = reinterpret_cast<uint16_t *>(a.ws + g.off_a) + tl.b * rp * rp;
-  uint16_t *B = reinterpret_cast<uint16_t *>(a.ws + g.off_b) + tl.b * rp * rp;
+  // a split group keeps B as [B_hi | B_lo], row pitch 2 rp (one 128-tile: tm = tn = 0)
+  const bool split = C::TM == kNsSmall && g.split;
+  const int64_t ldb = split ? 2 * rp : rp;
+  uint16_t *B = reinterpret_cast<uint16_t *>(a.ws + g.off_b) + tl.b * rp * ldb;
   const int r0 = tl.tm * TILE, c0 = tl.tn * TILE;
   f32x16_t acc[C::MBM][C::MBN];
   if (STAGE == 0) {
@@ -596,20 +634,31 @@ __global__ __launch_bounds__(C::NT, C::NT == 256 ? 2 : 1) void k_ns(NsArgs a) {
     // B = c (A A + (b/c) A); the A term is Q^T = A[c0.., r0..]^T, taken from LDS
     gemm_core<C, true>(reinterpret_cast<const char *>(A + r0 * rp), reinterpret_cast<const char *>(A + c0 * rp),
                        rp, smem, acc, r0, a.cb / a.cc);
-    store_tile<C, CACHED>(acc, a.cc, 0.f, nullptr, 0, B, rp, tl.tm != tl.tn ? B : nullptr, rp, r0, c0, smem);
+    if (split)
+      store_tile<C, CACHED>(acc, a.cc, 0.f, nullptr, 0, B, ldb, nullptr, 0, r0, c0, smem, B + rp);
+    else
+      store_tile<C, CACHED>(acc, a.cc, 0.f, nullptr, 0, B, rp, tl.tm != tl.tn ? B : nullptr, rp, r0, c0, smem);
   } else {
     const uint16_t *XTc = (a.iter & 1) ? XT1 : XT0;
     uint16_t *XTn = (a.iter & 1) ? XT0 : XT1;
     // X' = al (B X + a X): the a X term is taken from the Q operand in LDS
     const float al = a.iter == 0 ? s : 1.f;
-    if (STAGE == 2) {
+    auto update = [&]() __attribute__((always_inline)) {
+      if constexpr (C::TM == kNsSmall) {
+        if (split) {
+          gemm_core<C, true, false, true>(reinterpret_cast<const char *>(B + r0 * ldb),
+                                          reinterpret_cast<const char *>(XTc + c0 * rp), ldb, smem, acc, r0, a.ca);
+          return;
+        }
+      }
       gemm_core<C, true>(reinterpret_cast<const char *>(B + r0 * rp),
                          reinterpret_cast<const char *>(XTc + c0 * rp), rp, smem, acc, r0, a.ca);
+    };
+    if (STAGE == 2) {
+      update();
       store_tile<C, CACHED>(acc, al, 0.f, nullptr, 0, X, cp, XTn, rp, r0, c0, smem);
     } else {
-      if (!zero)
-        gemm_core<C, true>(reinterpret_cast<const char *>(B + r0 * rp),
-                           reinterpret_cast<const char *>(XTc + c0 * rp), rp, smem, acc, r0, a.ca);
+      if (!zero) update();
       const MuonUnit u = a.units[unit];
       final_tile<C>(acc, al, u, a.w, a.lr, a.decay, r0, c0, zero, smem);
     }

@@ -206,6 +206,12 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
       // read X row-major.
       const bool km_fits = ((int64_t)g.c_pad - 1) * g.r_pad * 2 + kNsLarge * 2 <= (int64_t)0x7FFFFFFF;
       g.km = g.g256 == 0 && km_fits && !(p.opts.flags & SSHDP_PLAN_NS_GRAM_NT) ? 1 : 0;
+      // One 128-row tile in r (per-head units, small matrices): B goes to memory as a pair of
+      // bf16 matrices, its rounding and the remainder, and the update contracts over both
+      // (K = 2 r_pad).  Rounding B to bf16 is the largest of the iteration's storage errors
+      // (a 32 x 507 unit: 2.4e-2 from the float64 iteration with B in bf16, 1.2e-2 with the
+      // pair); the doubled K costs these short-K, latency-bound updates little.
+      g.split = g.r_pad == kNsSmall ? 1 : 0;
     }
     g.n = (int32_t)kv.second.size();
     g.unit_base = (int32_t)p.munits.size();
@@ -246,7 +252,7 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
     g.off_xt0 = off; off = round_up(off + xs, kAlign);
     g.off_xt1 = off; off = round_up(off + xs, kAlign);
     g.off_a = off;   off = round_up(off + as, kAlign);
-    g.off_b = off;   off = round_up(off + as, kAlign);
+    g.off_b = off;   off = round_up(off + (g.split ? 2 * as : as), kAlign);
     for (int32_t k = 0; k < g.n; ++k) {
       MuonUnit &u = p.munits[g.unit_base + k];
       const int64_t ux = (int64_t)g.off_x + (int64_t)k * g.r_pad * g.c_pad * 2;
@@ -266,7 +272,8 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
     const double tri = n2 * (n2 + 1) / 2 * L * L + ((n1 * (n1 + 1) - s1 * (s1 + 1)) / 2) * S * S;
     const double u2 = (double)(g.u256r / kNsLarge) * (g.u256c / kNsLarge) * L * L;
     const double u1 = ((double)g.r_pad * g.c_pad - (double)g.u256r * g.u256c);
-    cost[gi] = g.n * (tri * 2.0 * (g.c_pad + g.r_pad) + (u2 + u1) * 2.0 * g.r_pad);
+    cost[gi] = g.n * (tri * 2.0 * (g.c_pad + g.r_pad) + (u2 + u1) * 2.0 * g.r_pad * (g.split ? 2 : 1));
+    p.group_unit_flops.push_back(cost[gi] / g.n * p.opts.ns_steps);
   }
   std::vector<size_t> order(p.groups.size());
   for (size_t i = 0; i < order.size(); ++i) order[i] = i;
@@ -339,7 +346,7 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
   for (size_t gi = 0; gi < p.groups.size(); ++gi) {
     const Group &g = p.groups[gi];
     p.ns_groups.push_back({(int64_t)g.off_x, (int64_t)g.off_xt0, (int64_t)g.off_xt1, (int64_t)g.off_a,
-                           (int64_t)g.off_b, g.r_pad, g.c_pad, g.unit_base, g.n, g.km, 0});
+                           (int64_t)g.off_b, g.r_pad, g.c_pad, g.unit_base, g.n, g.km, g.split});
     const int ln = p.group_lane[gi];
     const int n2 = g.g256 / kNsLarge, n1 = g.r_pad / kNsSmall, s1 = g.g256 / kNsSmall;
     const int ur2 = g.u256r / kNsLarge, uc2 = g.u256c / kNsLarge;
@@ -375,8 +382,10 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
         });
         xcd_order(v, p.groups, st == 0, st == 2);
         const double t = sz ? kNsLarge : kNsSmall;
-        for (const NsTile &x : v)
-          p.stats.ns_tile_flops += t * t * 2.0 * (st == 0 ? p.groups[x.group].c_pad : p.groups[x.group].r_pad);
+        for (const NsTile &x : v) {
+          const Group &gx = p.groups[x.group];
+          p.stats.ns_tile_flops += t * t * 2.0 * (st == 0 ? gx.c_pad : st == 2 && gx.split ? 2 * gx.r_pad : gx.r_pad);
+        }
       }
   p.stats.ns_tile_flops *= p.opts.ns_steps;
   p.stats.n_muon_units = (int32_t)p.munits.size();
@@ -631,6 +640,8 @@ int sshdp_plan_group(const sshdp_plan *p, int32_t g, sshdp_group_info *info) {
   info->n_units = G.n; info->tile = G.u256r ? kNsLarge : kNsSmall; info->tile_gram = G.g256 ? kNsLarge : kNsSmall;
   info->gram256 = G.g256; info->upd256_rows = G.u256r; info->upd256_cols = G.u256c;
   info->gram_kmajor = G.km;
+  info->split_b = G.split;
+  info->lane = p->group_lane[g];
   return SSHDP_OK;
 }
 

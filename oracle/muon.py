@@ -38,10 +38,12 @@ def momentum_step(m, g, mu, nesterov=False):
     return m_new, bf16_rne(src)
 
 
-def newton_schulz(u, steps=5, a=3.4445, b=-4.7750, c=2.0315, eps=1e-7):
+def newton_schulz(u, steps=5, a=3.4445, b=-4.7750, c=2.0315, eps=1e-7, progress=None):
     """f1: quintic Newton-Schulz orthogonalisation of u (any 2-D shape), float64.
 
     The coefficients arrive as the float32 values the library receives.
+    ``progress`` (optional) is called with the step number after each step
+    (long runs on large units report as they go).
     """
     a, b, c = (np.float64(np.float32(t)) for t in (a, b, c))
     eps = np.float64(np.float32(eps))
@@ -50,10 +52,12 @@ def newton_schulz(u, steps=5, a=3.4445, b=-4.7750, c=2.0315, eps=1e-7):
     if tall:
         X = X.T
     X = X / (np.sqrt(np.sum(X * X)) + eps)
-    for _ in range(steps):
+    for k in range(steps):
         A = X @ X.T
         B = b * A + c * (A @ A)
         X = a * X + B @ X
+        if progress is not None:
+            progress(k + 1)
     return X.T if tall else X
 
 

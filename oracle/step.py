@@ -1,8 +1,8 @@
 """One update step over a packed root: Muon units, AdamW units, then G.
 
-[SS-HSDP §3.4, "Update"]: after the microbatches, each unit's F runs (for
-Muon: f0, f1, f2) and applying G to the updated main weights begins the next
-cycle.  [SS-HSDP §4.1]: compatible operations are batched; batching changes
+[SS-HSDP §3.4, "Update"]: once the microbatches are done every unit runs its
+F (for Muon: f0, f1, f2), and G, run on the new main weights, produces the
+runtime weights the next iteration uses.  [SS-HSDP §4.1]: compatible operations are batched; batching changes
 launch count, not the result, so the oracle simply loops over units.  Muon and
 AdamW units own disjoint elements (checked by resolve_views), so their order
 does not matter; G reads every updated weight, so it runs last.

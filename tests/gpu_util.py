@@ -68,28 +68,16 @@ def oracle_step(wl, layout, w, g, m, v, step=1, hp=None, **kw):
     return dict(w=w, m=m, v=v, codes=codes, scales=scales), dirs
 
 
-def ns_bf16_model(u, steps=5, a=3.4445, b=-4.7750, c=2.0315, eps=1e-7):
-    """The Newton-Schulz iteration with the kernels' storage points rounded to
-    bf16 (A, B and every X but the last; products in float64, which stands in
-    for the kernels' fp32 accumulation), the normalisation folded into the
-    first step's scalars as the kernels do.  A model of the bf16 method, not
-    the oracle: it shows how far bf16 storage alone moves a unit's direction
-    from the float64 iteration, which bounds what any bf16 computation of that
-    unit can reach.  u: the bf16 momentum of one unit in its own layout."""
-    bf = lambda x: oracle.bf16_rne(np.asarray(x, np.float32)).astype(np.float64)
-    a, b, c = (np.float64(np.float32(t)) for t in (a, b, c))
-    X = np.asarray(u, np.float64)
-    tall = X.shape[0] > X.shape[1]
-    if tall:
-        X = X.T
-    s = 1.0 / (np.sqrt(np.sum(X * X)) + np.float64(np.float32(eps)))
-    for k in range(steps):
-        al = s if k == 0 else 1.0
-        A = bf(al * al * (X @ X.T))
-        B = bf(c * (A @ A) + b * A)
-        Y = al * (B @ X + a * X)
-        X = Y if k + 1 == steps else bf(Y)
-    return X.T if tall else X
+def adam_elementwise_ok(w_gpu, w_ref, lr=ADAM["lr"]):
+    """The elementwise AdamW bound beside the normwise one: every element within
+    1e-6 of its own magnitude plus 4 float32 units of the step size,
+    |w_gpu - w_ref| <= 1e-6 |w_ref| + 4 lr 2^-24 (the additive term covers
+    elements near zero, where a relative bound alone is ill-posed).  Returns
+    the worst ratio of error to bound (<= 1 passes)."""
+    w_gpu = np.asarray(w_gpu, np.float64)
+    w_ref = np.asarray(w_ref, np.float64)
+    bound = 1e-6 * np.abs(w_ref) + 4.0 * np.float64(np.float32(lr)) * 2.0 ** -24
+    return float(np.max(np.abs(w_gpu - w_ref) / bound)) if w_ref.size else 0.0
 
 
 def rel_fro(a, b):

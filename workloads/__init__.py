@@ -12,7 +12,7 @@ block boundaries [veScale §5].
 
 Random numbers: numpy Generator(PCG64(SeedSequence([config_id, stream]))),
 stream 0 = main weights, 1 = gradients, 2 = structure (expert choice, ragged
-sizes).  w ~ N(0, 0.02^2), g ~ N(0, 1e-3^2), momentum and second moment zero,
+sizes), 16 + t = the fresh gradient of step t > 1 in multi-step tests.  w ~ N(0, 0.02^2), g ~ N(0, 1e-3^2), momentum and second moment zero,
 padding zero in every field.
 """
 
@@ -50,19 +50,31 @@ class Workload:
         if not self._arrays:
             w = rng(self.config_id, 0).standard_normal(self.root_numel, dtype=np.float32)
             w *= np.float32(W_STD)
-            g = rng(self.config_id, 1).standard_normal(self.root_numel, dtype=np.float32)
-            g *= np.float32(G_STD)
             for s, n in self.padding:
                 w[s:s + n] = 0
-                g[s:s + n] = 0
-            for i in self.zero_grad_units:
-                nd = self.nodes[i]
-                a = _abs_offset(self.nodes, i)
-                for r in range(nd["rows"]):
-                    s = a + r * nd["row_stride"]
-                    g[s:s + nd["cols"]] = 0
-            self._arrays = {"w": w, "g": g}
+            self._arrays = {"w": w, "g": self._draw_gradient(rng(self.config_id, 1))}
         return self._arrays["w"], self._arrays["g"]
+
+    def gradient(self, t):
+        """The gradient root of step t (t >= 1): step 1 is arrays()'s, every later
+        step a fresh draw from stream 16 + t, with the same zero padding and
+        zero-gradient units."""
+        if t == 1:
+            return self.arrays()[1]
+        return self._draw_gradient(rng(self.config_id, 16 + t))
+
+    def _draw_gradient(self, gen):
+        g = gen.standard_normal(self.root_numel, dtype=np.float32)
+        g *= np.float32(G_STD)
+        for s, n in self.padding:
+            g[s:s + n] = 0
+        for i in self.zero_grad_units:
+            nd = self.nodes[i]
+            a = _abs_offset(self.nodes, i)
+            for r in range(nd["rows"]):
+                s = a + r * nd["row_stride"]
+                g[s:s + nd["cols"]] = 0
+        return g
 
 
 def _abs_offset(nodes, i):
@@ -202,6 +214,18 @@ def mixed_tiles(cid=101, name="odd multiples of 128 (256-tile blocks with 128-ti
     t.region(130, 260, unit=True, opt="muon")
     t.region(1, 96, unit=True, opt="adamw", quant=True)
     return _finish(cid, name, t, "rowmajor")
+
+
+def long_k_units(cid=105, name="4096 x 4224 wide and 4224 x 4096 tall Muon units"):
+    """Two Muon units of one oriented shape, r = 4096, c = 4224: large enough
+    that the default plan runs the Gram and polynomial in 256-tiles (with a
+    128 strip, c_pad = 4224) and the update with K = 4096, the long-K update's
+    tile order; small enough for the float64 oracle (about 2 TFLOP each)."""
+    t = _Tree()
+    t.region(4096, 4224, unit=True, opt="muon", quant=True)
+    t.region(4224, 4096, unit=True, opt="muon", quant=True)
+    t.region(1, 4096, unit=True, opt="adamw")
+    return _finish(cid, name, t, "tile32x4")
 
 
 def random_units(cid=102, n=6, name="random Muon shapes"):
