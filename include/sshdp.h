@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SSHDP_ABI_VERSION 5
+#define SSHDP_ABI_VERSION 6
 
 /* Status codes.  The planning errors are the rejections of [SS-HSDP Appendix A,
  * Table 4]: incompatible metadata, invalid geometry, storage overlap. */
@@ -66,7 +66,8 @@ enum {
   SSHDP_ERR_ALIGN = -6,     /* a device pointer is not 16-byte aligned                 */
   SSHDP_ERR_WORKSPACE = -7, /* workspace missing or smaller than sshdp_plan_info says  */
   SSHDP_ERR_HIP = -8,       /* a HIP runtime call or kernel launch failed              */
-  SSHDP_ERR_STATE = -9      /* the plan was made host-only and cannot launch           */
+  SSHDP_ERR_STATE = -9,     /* the plan was made host-only and cannot launch           */
+  SSHDP_ERR_SCRATCH = -10   /* the plan needs more workspace than the built-in scratch  */
 };
 
 enum { SSHDP_OPT_NONE = 0, SSHDP_OPT_MUON = 1, SSHDP_OPT_ADAMW = 2 };
@@ -324,6 +325,24 @@ int sshdp_rs_accumulate(const void *const *inputs, int32_t n_inputs, int32_t in_
 int sshdp_update_step(const sshdp_plan *plan, const sshdp_buffers *bufs, const sshdp_muon_hp *mh,
                       const sshdp_adamw_hp *ah, int64_t step, void *workspace, size_t workspace_bytes,
                       void *stream);
+
+/* sshdp_update_step without caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a device array built
+ * into the library, SSHDP_NOALLOC_SCRATCH_BYTES (64 MiB) on every GPU the
+ * library runs on, held until the process ends; its address is looked up on
+ * the first call on each device.  The call allocates nothing (with
+ * sshdp_profile_enable on, its timing events are created on first use, as in
+ * every launching call).  Plans whose stats.workspace_bytes exceed the array
+ * are refused (SSHDP_ERR_SCRATCH) before anything is launched.  Every call on
+ * a GPU shares that GPU's array and leaves its contents behind (nothing in it
+ * needs to start at zero: each step writes the whole region it reads), so
+ * calls that may overlap on one GPU -- on different streams or from different
+ * threads -- race; order them on one stream.  Otherwise it is exactly
+ * sshdp_update_step: same arguments, results and other errors. */
+#define SSHDP_NOALLOC_SCRATCH_BYTES (64u << 20)
+int sshdp_update_step_noalloc(const sshdp_plan *plan, const sshdp_buffers *bufs, const sshdp_muon_hp *mh,
+                              const sshdp_adamw_hp *ah, int64_t step, void *stream);
 
 /* Diagnostics.  The batched NT contraction used by Newton-Schulz, exposed to
  * test it alone: for b < batch, O[b] = bf16(alpha * P[b] Q[b]^T + beta * D[b])

@@ -7,5 +7,5 @@ include/sshdp.h.  This package is the thin ctypes binding of that library.
 from ._lib import (  # noqa: F401
     LIB_PATH, SshdpError, Plan, buffers, muon_hp, adamw_hp, update_muon, update_adamw, requant_mxfp8,
     cast_bf16, rs_reduce, rs_accumulate,
-    update_step, gemm_bf16_nt, lib, PROF_CLASSES, ERROR_NAMES,
+    update_step, update_step_noalloc, gemm_bf16_nt, lib, PROF_CLASSES, ERROR_NAMES, NOALLOC_SCRATCH_BYTES,
 )

@@ -14,11 +14,12 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsshdp.so")
 
-OK, ERR_ARG, ERR_TREE, ERR_BOUNDS, ERR_OVERLAP, ERR_SCHEMA, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_STATE = \
-    0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+OK, ERR_ARG, ERR_TREE, ERR_BOUNDS, ERR_OVERLAP, ERR_SCHEMA, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_STATE, \
+    ERR_SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
 ERROR_NAMES = {ERR_ARG: "ARG", ERR_TREE: "TREE", ERR_BOUNDS: "BOUNDS", ERR_OVERLAP: "OVERLAP",
                ERR_SCHEMA: "SCHEMA", ERR_ALIGN: "ALIGN", ERR_WORKSPACE: "WORKSPACE", ERR_HIP: "HIP",
-               ERR_STATE: "STATE"}
+               ERR_STATE: "STATE", ERR_SCRATCH: "SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20    # SSHDP_NOALLOC_SCRATCH_BYTES
 OPT = {None: 0, "muon": 1, "adamw": 2}
 LAYOUT = {"rowmajor": 0, "tile32x4": 1, "block32x32": 2}
 PLAN_HOST_ONLY = 1
@@ -26,7 +27,7 @@ PLAN_HOST_ONLY = 1
 NS_TILES = {"auto": 0, "small": 2, "large": 4}
 # Gram operand: planner default (128-tile Grams read X^T), or X row-major for every Gram
 NS_GRAM = {"auto": 0, "nt": 8}
-ABI_VERSION = 5                     # SSHDP_ABI_VERSION of the header this binding follows
+ABI_VERSION = 6                     # SSHDP_ABI_VERSION of the header this binding follows
 PROF_CLASSES = ["momentum", "norm", "ns_gram", "ns_poly", "ns_update", "adamw", "adamw_requant", "requant",
                 "ns_phase", "cast_bf16", "lane0_gram", "lane0_poly", "lane0_update", "lane0_update_last"]
 # node["quantize"]: False/None (no G), True or "mxfp8" (MXFP8 codes + scales), "bf16" (bfloat16 cast)
@@ -111,6 +112,8 @@ SIGNATURES = {
                             ctypes.c_int),
     "sshdp_update_step": ([_P, ctypes.POINTER(Buffers), ctypes.POINTER(MuonHP), ctypes.POINTER(AdamWHP),
                            ctypes.c_int64, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "sshdp_update_step_noalloc": ([_P, ctypes.POINTER(Buffers), ctypes.POINTER(MuonHP), ctypes.POINTER(AdamWHP),
+                                   ctypes.c_int64, _P], ctypes.c_int),
     "sshdp_gemm_bf16_nt": ([_P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                             ctypes.c_float, ctypes.c_float, ctypes.c_int32, _P], ctypes.c_int),
     "sshdp_ns_executed": ([_P, _P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double),
@@ -326,6 +329,12 @@ def update_step(plan, bufs, mhp, ahp, step, workspace, workspace_bytes, stream=N
     _check(lib().sshdp_update_step(plan.handle, ctypes.byref(bufs), _ref(mhp), _ref(ahp),
                                    int(step), _ptr(workspace), int(workspace_bytes), _stream(stream)),
            "sshdp_update_step")
+
+
+def update_step_noalloc(plan, bufs, mhp, ahp, step, stream=None):
+    """sshdp_update_step with the library's built-in scratch as workspace."""
+    _check(lib().sshdp_update_step_noalloc(plan.handle, ctypes.byref(bufs), _ref(mhp), _ref(ahp), int(step),
+                                           _stream(stream)), "sshdp_update_step_noalloc")
 
 
 def gemm_bf16_nt(P, Q, D, O, OT, M, N, K, batch, alpha, beta, tile, stream=None):

@@ -569,6 +569,7 @@ const char *sshdp_status_string(int code) {
     case SSHDP_ERR_WORKSPACE: return "workspace missing or too small";
     case SSHDP_ERR_HIP: return "HIP runtime error";
     case SSHDP_ERR_STATE: return "plan is host-only";
+    case SSHDP_ERR_SCRATCH: return "plan needs more workspace than the built-in scratch holds";
     default: return "unknown status";
   }
 }

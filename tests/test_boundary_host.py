@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
         assert name in _lib.SIGNATURES, name
     assert set(_lib.SIGNATURES) == set(decl)
-    assert L.sshdp_abi_version() == 5
+    assert L.sshdp_abi_version() == 6
     assert L.sshdp_status_string(-5) == b"geometry or metadata the kernels cannot take"
 
 
