@@ -69,6 +69,8 @@ def parse():
                     help="Newton-Schulz tile policy of the plan (default: the planner's choice)")
     ap.add_argument("--ns-gram", choices=["auto", "nt"], default="auto",
                     help="Gram operand: the planner's choice (X^T for 128-tile Grams) or X row-major everywhere")
+    ap.add_argument("--ns-streams", choices=["auto", "one"], default="auto",
+                    help="Newton-Schulz groups on the planner's streams, or every group on the launch stream")
     ap.add_argument("--g", choices=["mxfp8", "bf16"], default="mxfp8",
                     help="G on the runtime weights: MXFP8 requant (default) or a bfloat16 cast")
     ap.add_argument("--cpu-budget", type=float, default=25.0, help="seconds of oracle work to aim for")
@@ -300,7 +302,8 @@ class Setup:
         nodes = wl.nodes
         if g_mode == "bf16":                      # every G region becomes a bfloat16 cast
             nodes = [dict(nd, quantize="bf16") if nd["quantize"] else nd for nd in nodes]
-        self.plan = sh.Plan(nodes, wl.root_numel, layout=self.layout, ns_tiles=args.ns_tiles, ns_gram=args.ns_gram)
+        self.plan = sh.Plan(nodes, wl.root_numel, layout=self.layout, ns_tiles=args.ns_tiles, ns_gram=args.ns_gram,
+                            ns_streams=getattr(args, "ns_streams", "auto"))
         self.st = self.plan.stats()
         self.w = torch.from_numpy(w0).to(dev)
         self.g = torch.from_numpy(g0).to(dev)
@@ -400,22 +403,20 @@ def main():
     roofline = ns_phase = None
     if st["n_muon_units"]:
         units_nz, exec_flops = S.plan.ns_executed(S.ws, S.ws_bytes, sp)
-        # the dominant kernel: the update product of the groups on the launch stream (steps before the
-        # last); executed MFMA flops per launch = 2 r_pad^2 c_pad per non-zero unit (twice that where B is
-        # held as a bf16 pair)
+        # the dominant kernel: the 256-tile launch of the update product on the launch stream (steps
+        # before the last); executed MFMA flops per launch = 2 r_pad per output element of the groups'
+        # 256-tile regions, for every unit whose momentum is not all zero
         lane0 = [i for i, gi in enumerate(groups) if gi["lane"] == 0]
-        upd_flops = sum(units_nz[i] * 2.0 * groups[i]["r_pad"] ** 2 * groups[i]["c_pad"] *
-                        (2 if groups[i]["split_b"] else 1) for i in lane0)
+        upd_flops = sum(units_nz[i] * 2.0 * groups[i]["upd256_rows"] * groups[i]["upd256_cols"] * groups[i]["r_pad"]
+                        for i in lane0)
         ms_upd, n_upd = prof["lane0_update"]
         if n_upd and upd_flops > 0:
             ms_launch = ms_upd / n_upd
             achieved = upd_flops / (ms_launch / 1e3) / 1e12
-            names = ", ".join(f"{groups[i]['r']}x{groups[i]['c']} x{groups[i]['n_units']}" for i in lane0)
-            tiles = "256-tiles" if all(groups[i]["tile"] == 256 and groups[i]["upd256_rows"] == groups[i]["r_pad"]
-                                       and groups[i]["upd256_cols"] == groups[i]["c_pad"] for i in lane0) \
-                else "256- and 128-tiles"
+            names = ", ".join(f"{groups[i]['r']}x{groups[i]['c']} x{groups[i]['n_units']}" for i in lane0
+                              if groups[i]["upd256_rows"])
             roofline = {"bound": "mfma",
-                        "kernel": f"k_ns update X' = aX + BX ({tiles}; groups {names}; launch stream)",
+                        "kernel": f"k_ns<2, 256-tile> update X' = aX + BX (groups {names}; launch stream)",
                         "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                         "traffic": measured_traffic(wl.name, "dominant"),
@@ -484,11 +485,16 @@ def main():
                    "muon_units": st["n_muon_units"], "adamw_units": st["n_adamw_units"],
                    "ns_groups": [[gi["r"], gi["c"], gi["n_units"]] for gi in groups],
                    "scale_layout": layout, "g": args.g, "ns_tiles": args.ns_tiles, "ns_gram": args.ns_gram,
+                   "ns_streams": args.ns_streams,
                    "ns_tflop_per_step": st["ns_flops"] / 1e12,
                    "repack_workload": repack_wl.name if repack_wl is not None else None},
         "roofline": roofline, "ns_phase": ns_phase, "repack_roofline": repack, "g_roofline": g_roof,
         "cast_roofline": cast, "components": components, "graph_ms_per_step": graph_ms,
     }
+    if roofline is None and ns_phase is not None:      # no 256-tile update launch (small workloads)
+        roofline = dict(ns_phase, kernel="k_ns (every Newton-Schulz launch, NS phase wall time)",
+                        traffic=measured_traffic(wl.name, "dominant"))
+    out["roofline"] = roofline
     out["env"] = run_env(torch, wl)
     if not args.no_cpu:
         cb = cpu_baseline(wl, args.cpu_budget)

@@ -98,12 +98,16 @@ enum { SSHDP_SCALE_ROWMAJOR = 0, SSHDP_SCALE_TILE32X4 = 1, SSHDP_SCALE_BLOCK32X3
  * leading block when the group is large enough to fill the GPU with them, and
  * in 128 x 128 tiles elsewhere.  Setting both tile flags is an argument error.
  * Gram products that run in 128-tiles read X^T (so only X^T is stored) unless
- * SSHDP_PLAN_NS_GRAM_NT is set or X^T of the unit exceeds 2^31 bytes. */
+ * SSHDP_PLAN_NS_GRAM_NT is set or X^T of the unit exceeds 2^31 bytes.  Groups
+ * other than the largest run on side streams only while the largest group's
+ * launches fill fewer than two rounds of the GPU's workgroup slots in some
+ * stage; SSHDP_PLAN_NS_ONE_STREAM keeps every group on the caller's stream. */
 enum {
   SSHDP_PLAN_HOST_ONLY = 1,       /* plan and validate on the host; no device tables (cannot launch) */
   SSHDP_PLAN_NS_TILES_SMALL = 2,  /* every Newton-Schulz product in 128 x 128 tiles                  */
   SSHDP_PLAN_NS_TILES_LARGE = 4,  /* 256 x 256 tiles over every 256-aligned leading block            */
-  SSHDP_PLAN_NS_GRAM_NT = 8       /* every Gram reads X row-major (X and X^T stored); for comparison */
+  SSHDP_PLAN_NS_GRAM_NT = 8,      /* every Gram reads X row-major (X and X^T stored); for comparison */
+  SSHDP_PLAN_NS_ONE_STREAM = 16   /* every Newton-Schulz group on the caller's stream, none on side streams */
 };
 
 /* One data-tree node [SS-HSDP §3.2]: a 2-D view (rows x cols, cols contiguous,
@@ -382,7 +386,8 @@ int sshdp_ns_executed(const sshdp_plan *plan, const void *workspace, size_t work
  * different groups run concurrently on plan-owned streams, so classes 2-4 can
  * overlap in time), 9 G bf16 cast, and the Newton-Schulz launches of the
  * caller's stream alone (the groups whose sshdp_group_info.lane is 0): 10 Gram,
- * 11 poly, 12 update of the steps before the last, 13 the last update (+f2).
+ * 11 poly (both tile sizes), 12 the update's 256-tile launch in the steps
+ * before the last, 13 that launch in the last step (+f2).
  * Not thread-safe; for measurement only. */
 enum { SSHDP_PROF_CLASSES = 14 };
 int sshdp_profile_enable(sshdp_plan *plan, int32_t enable);

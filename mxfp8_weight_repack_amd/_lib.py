@@ -27,6 +27,7 @@ PLAN_HOST_ONLY = 1
 NS_TILES = {"auto": 0, "small": 2, "large": 4}
 # Gram operand: planner default (128-tile Grams read X^T), or X row-major for every Gram
 NS_GRAM = {"auto": 0, "nt": 8}
+NS_STREAMS = {"auto": 0, "one": 16}
 ABI_VERSION = 6                     # SSHDP_ABI_VERSION of the header this binding follows
 PROF_CLASSES = ["momentum", "norm", "ns_gram", "ns_poly", "ns_update", "adamw", "adamw_requant", "requant",
                 "ns_phase", "cast_bf16", "lane0_gram", "lane0_poly", "lane0_update", "lane0_update_last"]
@@ -196,14 +197,17 @@ class Plan:
     """A resolved data tree (sshdp_plan_views) and its tables."""
 
     def __init__(self, nodes, root_numel, layout="rowmajor", ns_steps=5, ns_a=3.4445, ns_b=-4.7750, ns_c=2.0315,
-                 ns_eps=1e-7, nesterov=False, scale_mode=0, host_only=False, ns_tiles="auto", ns_gram="auto"):
+                 ns_eps=1e-7, nesterov=False, scale_mode=0, host_only=False, ns_tiles="auto", ns_gram="auto",
+                 ns_streams="auto"):
         o = default_opts()
         o.ns_steps, o.ns_a, o.ns_b, o.ns_c, o.ns_eps = ns_steps, ns_a, ns_b, ns_c, ns_eps
         o.scale_layout = LAYOUT[layout]
         o.nesterov = int(bool(nesterov))
         o.muon_scale_mode = scale_mode
         # an unknown policy sets both tile flags, which the library rejects (ARG)
-        o.flags = (PLAN_HOST_ONLY if host_only else 0) | NS_TILES.get(ns_tiles, 6) | NS_GRAM.get(ns_gram, 16)
+        # (an unknown gram or stream value sets a flag bit the library does not define: ARG as well)
+        o.flags = (PLAN_HOST_ONLY if host_only else 0) | NS_TILES.get(ns_tiles, 6) | NS_GRAM.get(ns_gram, 1 << 30) \
+            | NS_STREAMS.get(ns_streams, 1 << 30)
         self._nodes = node_array(nodes)
         self._h = ctypes.c_void_p()
         self.layout = layout

@@ -139,8 +139,22 @@ int run_muon(const sshdp_plan *p, const sshdp_buffers *b, const sshdp_muon_hp *h
       for (int ln = 0; ln < p->n_lanes; ++ln) {
         hipStream_t ls = ln == 0 ? s : p->lane_stream[ln];
         Prof pr(p, 2 + stage, ls);
-        Prof pr0(p, ln == 0 ? 10 + kind : -1, ls);       // the caller's stream's launches alone
-        e = launch_ns_stage(*p, ln, kind, it, w, b->w_main, hp->lr, hp->weight_decay, ls);
+        if (ln == 0 && p->prof) {
+          // the caller's stream's launches alone: Gram and poly per stage, the update's
+          // 256-tile launch on its own (then its 128-tile launch, untimed)
+          if (kind < 2) {
+            Prof pr0(p, 10 + kind, ls);
+            e = launch_ns_stage(*p, ln, kind, it, w, b->w_main, hp->lr, hp->weight_decay, ls);
+          } else {
+            {
+              Prof pr0(p, 10 + kind, ls);
+              e = launch_ns_stage(*p, ln, kind, it, w, b->w_main, hp->lr, hp->weight_decay, ls, 1);
+            }
+            if (e == hipSuccess) e = launch_ns_stage(*p, ln, kind, it, w, b->w_main, hp->lr, hp->weight_decay, ls, 2);
+          }
+        } else {
+          e = launch_ns_stage(*p, ln, kind, it, w, b->w_main, hp->lr, hp->weight_decay, ls);
+        }
         if (e != hipSuccess) return SSHDP_ERR_HIP;
       }
     }
@@ -316,11 +330,12 @@ int sshdp_gemm_bf16_nt(const void *P, const void *Q, const void *D, void *O, voi
   if (!P || !Q || !O || M <= 0 || N <= 0 || K <= 0 || batch <= 0) return SSHDP_ERR_ARG;
   if (tile != 128 && tile != 256 && tile != 1281 && tile != 2561) return SSHDP_ERR_ARG;
   const int tt = tile == 1281 ? 128 : tile == 2561 ? 256 : tile;
+  const bool kmajor = tile == 1281 || tile == 2561;
   if (M % tt || N % tt || K % 64) return SSHDP_ERR_SCHEMA;
   // each operand panel is one buffer resource with 32-bit byte offsets
-  const int64_t span = tt == tile ? (int64_t)tt * K * 2 : ((int64_t)K - 1) * M * 2 + (int64_t)tt * 2;
+  const int64_t span = !kmajor ? (int64_t)tt * K * 2 : ((int64_t)K - 1) * M * 2 + (int64_t)tt * 2;
   if (span > 0x7FFFFFFF) return SSHDP_ERR_SCHEMA;
-  if (tt != tile && (D || M != N)) return SSHDP_ERR_ARG;
+  if (kmajor && (D || M != N)) return SSHDP_ERR_ARG;
   if (!aligned16(P) || !aligned16(Q) || (D && !aligned16(D)) || !aligned16(O) || (OT && !aligned16(OT)))
     return SSHDP_ERR_ALIGN;
   return hip_status(launch_gemm_raw(P, Q, D, O, OT, M, N, K, batch, alpha, D ? beta : 0.f, tile,

@@ -19,6 +19,7 @@ constexpr int kNsLarge = 256;        // ... or 256 x 256 (8 waves), chosen per g
 constexpr int64_t kNsMaxEdge = (int64_t)0x7FFFFFFF / (2 * kNsLarge) / kNsSmall * kNsSmall;
 constexpr int64_t kNsCacheBytes = 256ll << 20;  // last-level cache (MALL) of the chip
 constexpr int kMaxLanes = 4;         // Newton-Schulz groups run on up to 4 concurrent streams
+constexpr int kGpuCus = 256;         // compute units of an MI355X (workgroup slots for the stream rule)
 constexpr int kChunk = 4096;         // elements per AdamW / requant work item
 constexpr size_t kAlign = 256;       // workspace sub-buffer alignment (bytes)
 constexpr int kRsMaxInputs = 8;      // slices one reduce-scatter reduction call takes
@@ -177,9 +178,10 @@ namespace sshdp {
 hipError_t launch_f0(const sshdp_plan &p, int lane, const float *g, float *m, float mu, int nesterov, char *ws,
                      hipStream_t s);
 hipError_t launch_norm(const sshdp_plan &p, int lane, char *ws, float eps, hipStream_t s);
-// stage: 0 Gram, 1 poly, 2 update, 3 final update (+f2); one launch covers all groups
+// stage: 0 Gram, 1 poly, 2 update, 3 final update (+f2); one launch per tile size covers all
+// groups of the lane; sizes: 1 = the 256-tile launch, 2 = the 128-tile launch, 3 = both
 hipError_t launch_ns_stage(const sshdp_plan &p, int lane, int stage, int iter, char *ws, float *w_main, float lr,
-                           float wd, hipStream_t s);
+                           float wd, hipStream_t s, int sizes = 3);
 hipError_t launch_gemm_raw(const void *P, const void *Q, const void *D, void *O, void *OT, int M, int N,
                            int K, int batch, float alpha, float beta, int tile, hipStream_t s);
 hipError_t launch_adamw(const ASeg *segs, int64_t nseg, const sshdp_buffers &b, const sshdp_adamw_hp &hp,

@@ -719,14 +719,14 @@ hipError_t launch_list(const NsArgs &a, size_t n, bool cached, hipStream_t s) {
 }
 
 template <int STAGE>
-hipError_t launch_sizes(const sshdp_plan &p, NsArgs a, int ln, int st, hipStream_t s) {
+hipError_t launch_sizes(const sshdp_plan &p, NsArgs a, int ln, int st, hipStream_t s, int sizes) {
   hipError_t e = hipSuccess;
-  if (!p.ns_tiles[ln][st][1].empty()) {       // 256-tile work first: it is the long part
+  if ((sizes & 1) && !p.ns_tiles[ln][st][1].empty()) {       // 256-tile work first: it is the long part
     a.tiles = p.d.ns_tiles[ln][st][1];
     e = launch_list<STAGE, CLarge>(a, p.ns_tiles[ln][st][1].size(), p.ns_cached, s);
     if (e != hipSuccess) return e;
   }
-  if (!p.ns_tiles[ln][st][0].empty()) {
+  if ((sizes & 2) && !p.ns_tiles[ln][st][0].empty()) {
     a.tiles = p.d.ns_tiles[ln][st][0];
     e = launch_list<STAGE, CSmall>(a, p.ns_tiles[ln][st][0].size(), p.ns_cached, s);
   }
@@ -736,7 +736,7 @@ hipError_t launch_sizes(const sshdp_plan &p, NsArgs a, int ln, int st, hipStream
 }  // namespace
 
 hipError_t launch_ns_stage(const sshdp_plan &p, int lane, int stage, int iter, char *ws, float *w_main, float lr,
-                           float wd, hipStream_t s) {
+                           float wd, hipStream_t s, int sizes) {
   NsArgs a{};
   a.ws = ws;
   a.groups = p.d.ns_groups;
@@ -750,10 +750,10 @@ hipError_t launch_ns_stage(const sshdp_plan &p, int lane, int stage, int iter, c
   a.cc = p.opts.ns_c;
   a.iter = iter;
   switch (stage) {
-    case 0: return launch_sizes<0>(p, a, lane, 0, s);
-    case 1: return launch_sizes<1>(p, a, lane, 1, s);
-    case 2: return launch_sizes<2>(p, a, lane, 2, s);
-    default: return launch_sizes<3>(p, a, lane, 2, s);
+    case 0: return launch_sizes<0>(p, a, lane, 0, s, sizes);
+    case 1: return launch_sizes<1>(p, a, lane, 1, s, sizes);
+    case 2: return launch_sizes<2>(p, a, lane, 2, s, sizes);
+    default: return launch_sizes<3>(p, a, lane, 2, s, sizes);
   }
 }
 

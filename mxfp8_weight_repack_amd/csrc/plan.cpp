@@ -284,12 +284,33 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
   // fewer side kernels contending for the CUs at once (d=2048 block: the O
   // projection and the 24 heads on one side stream, 2.44 ms per step against
   // 2.47 on two).  Once kMaxLanes are open, the least-loaded lane takes the rest.
+  // When the largest group fills the GPU by itself, every group stays on lane 0.
   p.group_lane.assign(p.groups.size(), 0);
   p.n_lanes = 1;
   {
     std::vector<double> load(kMaxLanes, 0.0);
     if (!order.empty()) load[0] = cost[order[0]];
-    for (size_t k = 1; k < order.size(); ++k) {
+    // Side streams only pay off while the largest group's launches leave workgroup slots
+    // idle (fewer than two rounds of the GPU's slots in some stage: e.g. the d=2048 block's
+    // MLP Gram, 408 128-tiles in 512 slots).  When every stage of it fills the GPU at least
+    // twice over, side kernels only take CUs from it: the d=8192 block runs 2% faster per
+    // step with every group on the caller's stream (93.6 against 95.7 ms, same box), and the
+    // d=2048 block 5% slower (2.43 against 2.31 ms).
+    bool fills = !order.empty();
+    if (fills) {
+      const Group &g = p.groups[order[0]];
+      const int64_t n2 = g.g256 / kNsLarge, n1 = g.r_pad / kNsSmall, s1 = g.g256 / kNsSmall;
+      const int64_t tri256 = n2 * (n2 + 1) / 2 * g.n, tri128 = (n1 * (n1 + 1) - s1 * (s1 + 1)) / 2 * g.n;
+      const int64_t up256 = (int64_t)(g.u256r / kNsLarge) * (g.u256c / kNsLarge) * g.n;
+      const int64_t up128 = ((int64_t)g.r_pad * g.c_pad - (int64_t)g.u256r * g.u256c) / (kNsSmall * kNsSmall) * g.n;
+      // rounds of one stage's launches: 256-tiles one per CU, 128-tiles two per CU
+      auto rounds = [&](int64_t t256, int64_t t128) {
+        return (double)t256 / kGpuCus + (double)t128 / (2.0 * kGpuCus);
+      };
+      fills = rounds(tri256, tri128) >= 2.0 && rounds(up256, up128) >= 2.0;
+    }
+    const bool one = fills || (p.opts.flags & SSHDP_PLAN_NS_ONE_STREAM) != 0;
+    for (size_t k = 1; k < order.size() && !one; ++k) {
       const double c = cost[order[k]];
       int best = -1;
       for (int l = 1; l < p.n_lanes; ++l)
@@ -598,7 +619,7 @@ int sshdp_plan_views(const sshdp_node *nodes, int32_t n_nodes, int64_t root_nume
   if (o.ns_steps < 1 || o.ns_steps > 64 || (o.scale_layout != SSHDP_SCALE_ROWMAJOR &&
       o.scale_layout != SSHDP_SCALE_TILE32X4 && o.scale_layout != SSHDP_SCALE_BLOCK32X32) ||
       o.muon_scale_mode < 0 || o.muon_scale_mode > 2 ||
-      !(o.ns_eps >= 0.0f) || (o.flags & ~15u) ||
+      !(o.ns_eps >= 0.0f) || (o.flags & ~31u) ||
       ((o.flags & SSHDP_PLAN_NS_TILES_SMALL) && (o.flags & SSHDP_PLAN_NS_TILES_LARGE)))
     return SSHDP_ERR_ARG;
   std::vector<int64_t> abs, ext;

@@ -69,7 +69,7 @@ hipError_t launch_f0(const sshdp_plan &, int, const float *, float *, float, int
   return launched(s);
 }
 hipError_t launch_norm(const sshdp_plan &, int, char *, float, hipStream_t s) { return launched(s); }
-hipError_t launch_ns_stage(const sshdp_plan &, int, int, int, char *, float *, float, float, hipStream_t s) {
+hipError_t launch_ns_stage(const sshdp_plan &, int, int, int, char *, float *, float, float, hipStream_t s, int) {
   return launched(s);
 }
 hipError_t launch_gemm_raw(const void *, const void *, const void *, void *, void *, int, int, int, int, float, float,
