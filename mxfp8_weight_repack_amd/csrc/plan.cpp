@@ -385,9 +385,14 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
           p.ns_tiles[ln][0][0].push_back({(int32_t)gi, b, tm, tn});
           p.ns_tiles[ln][1][0].push_back({(int32_t)gi, b, tm, tn});
         }
-      // update: 256-tiles on [0, u256r) x [0, u256c), 128-tiles on the rest
-      for (int tm = 0; tm < ur2; ++tm)
-        for (int tn = 0; tn < uc2; ++tn) p.ns_tiles[ln][2][1].push_back({(int32_t)gi, b, tm, tn});
+      // update: 256-tiles on [0, u256r) x [0, u256c), 128-tiles on the rest.  The 256-tiles go
+      // column by column, so their super-tiles are dealt to the XCDs column-major: the XCDs
+      // working at one time share X^T column panels (each read once from HBM, the rest from
+      // the last-level cache) and cycle through B, which fits that cache (d=8192 block: 87.96
+      // against 89.5 ms per step with row-major super-tiles, the update launch 0.516 against
+      // 0.501 of bf16 peak, same box; d=2048 block 2.234 against 2.247 ms).
+      for (int tn = 0; tn < uc2; ++tn)
+        for (int tm = 0; tm < ur2; ++tm) p.ns_tiles[ln][2][1].push_back({(int32_t)gi, b, tm, tn});
       for (int tm = 0; tm < nr1; ++tm)
         for (int tn = 0; tn < nc1; ++tn)
           if (tm >= ur1 || tn >= uc1) p.ns_tiles[ln][2][0].push_back({(int32_t)gi, b, tm, tn});
