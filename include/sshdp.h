@@ -99,9 +99,11 @@ enum { SSHDP_SCALE_ROWMAJOR = 0, SSHDP_SCALE_TILE32X4 = 1, SSHDP_SCALE_BLOCK32X3
  * in 128 x 128 tiles elsewhere.  Setting both tile flags is an argument error.
  * Gram products that run in 128-tiles read X^T (so only X^T is stored) unless
  * SSHDP_PLAN_NS_GRAM_NT is set or X^T of the unit exceeds 2^31 bytes.  Groups
- * other than the largest run on side streams only while the largest group's
+ * other than the largest run on side streams while the largest group's
  * launches fill fewer than two rounds of the GPU's workgroup slots in some
- * stage; SSHDP_PLAN_NS_ONE_STREAM keeps every group on the caller's stream. */
+ * stage; otherwise only the groups with r_pad == 128 do (on one side stream)
+ * and the rest share the caller's stream.  SSHDP_PLAN_NS_ONE_STREAM keeps
+ * every group on the caller's stream. */
 enum {
   SSHDP_PLAN_HOST_ONLY = 1,       /* plan and validate on the host; no device tables (cannot launch) */
   SSHDP_PLAN_NS_TILES_SMALL = 2,  /* every Newton-Schulz product in 128 x 128 tiles                  */
