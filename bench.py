@@ -36,6 +36,7 @@ bounded sample of the main workload and extrapolates to one whole step.
 """
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -212,6 +213,22 @@ def cpu_baseline(wl, budget_s):
             "seconds": measured}
 
 
+def peak_clock_mhz():
+    """The device's peak engine clock as the HIP runtime reports it (the clock
+    it sustains under the large contractions is lower: see the MFMA counter
+    summaries, which derive it from GRBM_GUI_ACTIVE)."""
+    try:
+        # by its soname, so the runtime torch has already loaded is the one asked
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        v = ctypes.c_int(0)
+        # hipDeviceAttributeClockRate (= 5 in hip_runtime_api.h), in kHz
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) == 0:
+            return v.value // 1000
+    except OSError:  # pragma: no cover
+        pass
+    return None
+
+
 def run_env(torch, wl):
     """What the numbers were taken on: device, software versions, host cores
     and the input seeds."""
@@ -228,6 +245,7 @@ def run_env(torch, wl):
         pass
     return {"device": p.name, "gcn_arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
             "l2_bytes": getattr(p, "L2_cache_size", None), "hbm_gib": round(p.total_memory / 2 ** 30, 1),
+            "peak_sclk_mhz": peak_clock_mhz(),
             "torch": torch.__version__, "hip": torch.version.hip,
             "host_cores": cores, "host_cpu": cpu,
             "seeds": f"numpy PCG64(SeedSequence([{wl.config_id}, stream])), stream 0 = w, 1 = g, 2 = structure"}
