@@ -23,7 +23,11 @@
 // ds_read_b64_tr_b16 pairs), so their update stores X'^T alone and f0 stores
 // u^T alone.
 // A and B are symmetric: only tiles with tm <= tn are computed and each
-// off-diagonal tile is also stored mirrored.  The normalisation is folded into
+// off-diagonal tile is also stored mirrored.  Groups of one 128-row tile
+// (per-head units) keep B as a bf16 pair [B_hi | B_lo], B_lo the rounded
+// remainder, and their update contracts over both halves (K = 2 r_pad, X^T
+// read twice): rounding B is the iteration's largest storage error, and these
+// short-K updates are latency-bound, so the doubled K costs little.  The normalisation is folded into
 // the first step's scalars: with s = 1/(||u|| + eps), A0 = s^2 u u^T and
 // X1 = s (B0 u) + a s u.  A unit whose momentum is all zero has s = 0 and skips
 // every product (its direction is exactly zero).  A tall unit is iterated on
