@@ -294,7 +294,7 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
     // idle (fewer than two rounds of the GPU's slots in some stage: e.g. the d=2048 block's
     // MLP Gram, 408 128-tiles in 512 slots).  When every stage of it fills the GPU at least
     // twice over, side kernels only take CUs from it: the d=8192 block runs 2% faster per
-    // step with every group on the caller's stream (93.6 against 95.7 ms, same box), and the
+    // step with every group on the caller's stream (93.6 against 95.7 ms, same GPU), and the
     // d=2048 block 5% slower (2.43 against 2.31 ms).
     bool fills = !order.empty();
     if (fills) {
@@ -312,7 +312,7 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
     const bool one = (p.opts.flags & SSHDP_PLAN_NS_ONE_STREAM) != 0;
     // ... except groups that run in 128-tiles alone (r_pad == 128: per-head units), whose
     // short, latency-bound launches then run beside the big ones on one side stream (d=8192
-    // block: 89.36 against 89.92 ms per step, same box, the update launch unchanged)
+    // block: 89.36 against 89.92 ms per step, same GPU, the update launch unchanged)
     if (fills && !one) {
       for (size_t k = 1; k < order.size(); ++k)
         if (p.groups[order[k]].r_pad == kNsSmall) {
@@ -400,7 +400,7 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
       // working at one time share X^T column panels (each read once from HBM, the rest from
       // the last-level cache) and cycle through B, which fits that cache (d=8192 block: 87.96
       // against 89.5 ms per step with row-major super-tiles, the update launch 0.516 against
-      // 0.501 of bf16 peak, same box; d=2048 block 2.234 against 2.247 ms).
+      // 0.501 of bf16 peak, same GPU; d=2048 block 2.234 against 2.247 ms).
       for (int tn = 0; tn < uc2; ++tn)
         for (int tm = 0; tm < ur2; ++tm) p.ns_tiles[ln][2][1].push_back({(int32_t)gi, b, tm, tn});
       for (int tm = 0; tm < nr1; ++tm)
