@@ -229,3 +229,26 @@ def test_planner_argument_errors():
     assert e.value.name == "STATE"
     p.destroy()
     p.destroy()
+
+
+def test_planner_stream_rule_and_split_pairs():
+    """Newton-Schulz groups and the streams they run on.  The largest group is on
+    the caller's stream (lane 0).  While it leaves workgroup slots idle (the d=2048
+    block's MLP Gram), the other groups share one side stream; when it fills the
+    GPU at least twice over in every stage (the d=8192 block), only the per-head
+    groups (r_pad = 128) leave lane 0.  A one-stream plan keeps every group on
+    lane 0.  Exactly the groups of one 128-row tile hold B as a bf16 pair."""
+    def lanes(cid, streams="auto", small=False):
+        wl = workloads.config(cid, small=small)
+        p = sh.Plan(wl.nodes, wl.root_numel, layout=wl.scale_layout, host_only=True, ns_streams=streams)
+        gs = p.groups()
+        for g in gs:
+            assert g["split_b"] == (g["r_pad"] == 128), g
+        return {(g["r"], g["c"]): g["lane"] for g in gs}
+
+    assert lanes(2) == {(128, 2048): 1, (2048, 2048): 1, (2048, 8192): 0}
+    assert lanes(5) == {(128, 8192): 1, (8192, 8192): 0, (8192, 28672): 0}
+    assert lanes(3) == {(1408, 2048): 0}
+    assert lanes(5, small=True) == {(128, 512): 1, (512, 512): 1, (512, 1536): 0}
+    for cid in (1, 2, 3, 5):
+        assert set(lanes(cid, "one").values()) == {0}
