@@ -9,6 +9,13 @@
 // and the caller's stream waits on that event afterwards.
 //
 // Input: one tree in the format of host_planner_check.cpp (first record only).
+//
+// With a second argument "tiles", the program instead checks the Newton-Schulz
+// tile tables of every record in the file, for each tile policy: per unit, the
+// Gram and poly tiles cover each 128 x 128 cell of the upper triangle of
+// r_pad x r_pad exactly once (256-tiles count for their 2 x 2 cells, a diagonal
+// one for its 3 upper cells), the update tiles cover every cell of r_pad x c_pad
+// exactly once, and every tile of a group sits in its group's lane.
 #include <cstdio>
 #include <cstdint>
 #include <cstdlib>
@@ -122,9 +129,103 @@ bool joined(int caller, int *bad_stream) {
   }
   return true;
 }
+
+// 0 if every table covers its unit's cells exactly once; else prints the first
+// problem and returns nonzero.
+int check_tiles(const sshdp_plan &p, const char *what) {
+  for (size_t gi = 0; gi < p.groups.size(); ++gi) {
+    const sshdp::Group &g = p.groups[gi];
+    const int R = g.r_pad / sshdp::kNsSmall, C = g.c_pad / sshdp::kNsSmall;
+    for (int st = 0; st < 3; ++st) {
+      const int W = st == 2 ? C : R;
+      std::vector<int> cnt((size_t)g.n * R * W, 0);
+      for (int ln = 0; ln < sshdp::kMaxLanes; ++ln)
+        for (int sz = 0; sz < 2; ++sz)
+          for (const sshdp::NsTile &t : p.ns_tiles[ln][st][sz]) {
+            if (t.group != (int)gi) continue;
+            if (ln != p.group_lane[gi] || t.b < 0 || t.b >= g.n) {
+              std::printf("%s group %zu stage %d: tile (b %d) on lane %d, group lane %d\n", what, gi, st, t.b, ln,
+                          p.group_lane[gi]);
+              return 7;
+            }
+            const int k = sz ? 2 : 1;
+            for (int i = 0; i < k; ++i)
+              for (int j = 0; j < k; ++j) {
+                const int r = t.tm * k + i, c = t.tn * k + j;
+                if (st < 2 && (t.tm > t.tn || r > c)) continue;   // mirrored cells are not computed
+                if (r < 0 || c < 0 || r >= R || c >= W) {
+                  std::printf("%s group %zu stage %d: cell (%d, %d) outside %d x %d\n", what, gi, st, r, c, R, W);
+                  return 8;
+                }
+                ++cnt[((size_t)t.b * R + r) * W + c];
+              }
+          }
+      for (int b = 0; b < g.n; ++b)
+        for (int r = 0; r < R; ++r)
+          for (int c = st < 2 ? r : 0; c < W; ++c)
+            if (cnt[((size_t)b * R + r) * W + c] != 1) {
+              std::printf("%s group %zu stage %d unit %d: cell (%d, %d) covered %d times\n", what, gi, st, b, r, c,
+                          cnt[((size_t)b * R + r) * W + c]);
+              return 9;
+            }
+    }
+  }
+  return 0;
+}
+
+int tiles_mode(const char *path) {
+  FILE *f = std::fopen(path, "rb");
+  if (!f) return 2;
+  int trees = 0, plans = 0;
+  for (;; ++trees) {
+    int32_t n = 0, layout = 0;
+    int64_t root = 0;
+    uint32_t flags = 0;
+    if (std::fread(&n, 4, 1, f) != 1) break;
+    if (std::fread(&root, 8, 1, f) != 1 || std::fread(&layout, 4, 1, f) != 1 || std::fread(&flags, 4, 1, f) != 1 ||
+        n <= 0)
+      return 3;
+    std::vector<sshdp_node> nodes(n);
+    if (std::fread(nodes.data(), sizeof(sshdp_node), n, f) != (size_t)n) return 3;
+    const uint32_t policies[] = {0, SSHDP_PLAN_NS_TILES_SMALL, SSHDP_PLAN_NS_TILES_LARGE, SSHDP_PLAN_NS_GRAM_NT,
+                                 SSHDP_PLAN_NS_ONE_STREAM};
+    for (uint32_t pol : policies) {
+      sshdp_plan_opts o;
+      sshdp_default_opts(&o);
+      o.scale_layout = layout;
+      o.flags = flags | pol | SSHDP_PLAN_HOST_ONLY;
+      sshdp_plan *p = nullptr;
+      if (sshdp_plan_views(nodes.data(), n, root, &o, &p) != SSHDP_OK) continue;   // rejected trees have no tiles
+      // TILECHK_PLANT=drop|dup plants a mistake in the first non-empty table, to
+      // show the check sees a missing or a doubled tile
+      if (const char *plant = std::getenv("TILECHK_PLANT")) {
+        bool done = false;
+        for (int ln = 0; ln < sshdp::kMaxLanes && !done; ++ln)
+          for (int st = 0; st < 3 && !done; ++st)
+            for (int sz = 0; sz < 2 && !done; ++sz) {
+              std::vector<sshdp::NsTile> &v = p->ns_tiles[ln][st][sz];
+              if (v.empty()) continue;
+              if (plant[0] == 'd' && plant[1] == 'r') v.pop_back();
+              else v.push_back(v.front());
+              done = true;
+            }
+      }
+      char what[64];
+      std::snprintf(what, sizeof what, "tree %d flags %u", trees, o.flags);
+      const int rc = check_tiles(*p, what);
+      sshdp_plan_destroy(p);
+      if (rc) return rc;
+      ++plans;
+    }
+  }
+  std::fclose(f);
+  std::printf("ok trees %d plans %d\n", trees, plans);
+  return 0;
+}
 }  // namespace
 
 int main(int argc, char **argv) {
+  if (argc == 3 && std::strcmp(argv[2], "tiles") == 0) return tiles_mode(argv[1]);
   if (argc != 2) return 2;
   FILE *f = std::fopen(argv[1], "rb");
   if (!f) return 2;
