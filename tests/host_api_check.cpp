@@ -173,6 +173,74 @@ int check_tiles(const sshdp_plan &p, const char *what) {
   return 0;
 }
 
+// The elementwise work tables, for roots small enough to mark element by element:
+// f0 tiles cover each Muon unit's padded layout once and sit in its group's lane
+// range; AdamW segments cover the AdamW units' elements once (aseg_all), and so
+// do the unfused segments together with the fused requant chunks' [lo, hi);
+// requant chunks cover every quantised region once, fused chunks first.
+int check_elementwise(const sshdp_plan &p, const std::vector<sshdp_node> &nodes, const char *what) {
+  for (const sshdp::MuonUnit &u : p.munits) {
+    const int TR = u.Rp / sshdp::kF0Tile, TC = u.Cp / sshdp::kF0Tile;
+    std::vector<int> seen((size_t)TR * TC, 0);
+    const int ln = p.group_lane[u.group];
+    if (u.tile_begin < p.f0_lane[ln] || u.tile_end > p.f0_lane[ln + 1]) {
+      std::printf("%s: unit's f0 tiles outside its lane's range\n", what);
+      return 10;
+    }
+    for (int k = u.tile_begin; k < u.tile_end; ++k) {
+      const sshdp::F0Tile &t = p.f0tiles[k];
+      if (&p.munits[t.unit] != &u || t.tr < 0 || t.tr >= TR || t.tc < 0 || t.tc >= TC) {
+        std::printf("%s: f0 tile %d does not belong to its unit\n", what, k);
+        return 10;
+      }
+      ++seen[(size_t)t.tr * TC + t.tc];
+    }
+    for (int v : seen)
+      if (v != 1) {
+        std::printf("%s: an f0 tile covered %d times\n", what, v);
+        return 10;
+      }
+  }
+  if (p.root_numel > ((int64_t)1 << 27)) return 0;
+  const size_t N = (size_t)p.root_numel;
+  std::vector<uint8_t> want(N, 0), all(N, 0), upd(N, 0), quant(N, 0), qwant(N, 0);
+  for (size_t i = 0; i < nodes.size(); ++i) {
+    const sshdp_node &nd = nodes[i];
+    if (!nd.is_unit || nd.optimizer != SSHDP_OPT_ADAMW) continue;
+    const int64_t rs = nd.rows > 1 ? nd.row_stride : nd.cols;
+    for (int64_t r = 0; r < nd.rows; ++r)
+      for (int64_t c = 0; c < nd.cols; ++c) want[p.node_abs[i] + r * rs + c] = 1;
+  }
+  for (const sshdp::ASeg &g : p.aseg_all)
+    for (int64_t e = g.base; e < g.base + g.n; ++e) ++all[e];
+  for (const sshdp::ASeg &g : p.aseg_unfused)
+    for (int64_t e = g.base; e < g.base + g.n; ++e) ++upd[e];
+  for (size_t k = 0; k < p.qchunks.size(); ++k) {
+    const sshdp::QChunk &q = p.qchunks[k];
+    const sshdp::QRegion &rg = p.qregions[q.region];
+    const int64_t end = rg.abs + rg.rows * rg.cols;
+    const bool fused = (int64_t)k < p.n_qchunks_fused;
+    if (q.n <= 0 || q.n % 32 || q.base < rg.abs || q.base + q.n > end || q.lo < q.base || q.hi < q.lo ||
+        q.hi > q.base + q.n || (!fused && q.hi != q.lo) || q.row0 != (q.base - rg.abs) / rg.cols ||
+        q.col0 != (q.base - rg.abs) % rg.cols) {
+      std::printf("%s: requant chunk %zu malformed\n", what, k);
+      return 11;
+    }
+    for (int64_t e = q.base; e < q.base + q.n; ++e) ++quant[e];
+    for (int64_t e = q.lo; e < q.hi; ++e) ++upd[e];
+  }
+  for (const sshdp::QRegion &rg : p.qregions)
+    for (int64_t e = rg.abs; e < rg.abs + rg.rows * rg.cols; ++e) ++qwant[e];
+  for (size_t e = 0; e < N; ++e) {
+    if (all[e] != want[e] || upd[e] != want[e] || quant[e] != qwant[e] || qwant[e] > 1) {
+      std::printf("%s: element %zu: AdamW unit %d, segments %d, updated %d times, quantised %d (regions %d)\n", what,
+                  e, want[e], all[e], upd[e], quant[e], qwant[e]);
+      return 12;
+    }
+  }
+  return 0;
+}
+
 int tiles_mode(const char *path) {
   FILE *f = std::fopen(path, "rb");
   if (!f) return 2;
@@ -196,9 +264,19 @@ int tiles_mode(const char *path) {
       o.flags = flags | pol | SSHDP_PLAN_HOST_ONLY;
       sshdp_plan *p = nullptr;
       if (sshdp_plan_views(nodes.data(), n, root, &o, &p) != SSHDP_OK) continue;   // rejected trees have no tiles
-      // TILECHK_PLANT=drop|dup plants a mistake in the first non-empty table, to
-      // show the check sees a missing or a doubled tile
-      if (const char *plant = std::getenv("TILECHK_PLANT")) {
+      // TILECHK_PLANT=drop|dup plants a mistake in the first non-empty tile table,
+      // =seg doubles the first AdamW segment a step runs (or the first fused
+      // requant chunk), to show the checks see a missing or a doubled item
+      const char *plant = std::getenv("TILECHK_PLANT");
+      const bool plant_seg = plant && std::strcmp(plant, "seg") == 0;
+      if (plant_seg) {
+        if (!p->aseg_unfused.empty()) {
+          p->aseg_unfused.push_back(p->aseg_unfused.front());
+        } else if (p->n_qchunks_fused > 0) {
+          p->qchunks.insert(p->qchunks.begin(), p->qchunks.front());
+          ++p->n_qchunks_fused;
+        }
+      } else if (plant) {
         bool done = false;
         for (int ln = 0; ln < sshdp::kMaxLanes && !done; ++ln)
           for (int st = 0; st < 3 && !done; ++st)
@@ -212,7 +290,8 @@ int tiles_mode(const char *path) {
       }
       char what[64];
       std::snprintf(what, sizeof what, "tree %d flags %u", trees, o.flags);
-      const int rc = check_tiles(*p, what);
+      int rc = plant_seg ? 0 : check_tiles(*p, what);
+      if (!rc && (!plant || plant_seg)) rc = check_elementwise(*p, nodes, what);
       sshdp_plan_destroy(p);
       if (rc) return rc;
       ++plans;
