@@ -408,6 +408,34 @@ void build_muon(sshdp_plan &p, const sshdp_node *nodes, int32_t n) {
           if (tm >= ur1 || tn >= uc1) p.ns_tiles[ln][2][0].push_back({(int32_t)gi, b, tm, tn});
     }
   }
+  // A symmetric product whose 256-tiles end in a short last round (at most half the CUs busy
+  // in it) hands that round's worth of off-diagonal 256-tiles to the 128-tile launch that
+  // follows on the same stream, four 128-tiles each, so no round runs mostly empty.  Only
+  // where every 256-tile of the launch has the same contraction length (the poly always;
+  // the Gram when its groups share c).
+  for (int ln = 0; ln < p.n_lanes; ++ln)
+    for (int st = 0; st < 2; ++st) {
+      std::vector<NsTile> &v = p.ns_tiles[ln][st][1];
+      const size_t n = v.size(), rem = n % kGpuCus;
+      if (n <= (size_t)kGpuCus || rem == 0 || rem > (size_t)kGpuCus / 2) continue;
+      bool same_k = true;
+      for (const NsTile &t : v)
+        same_k &= (st == 0 ? p.groups[t.group].c_pad : p.groups[t.group].r_pad) ==
+                  (st == 0 ? p.groups[v[0].group].c_pad : p.groups[v[0].group].r_pad);
+      if (!same_k) continue;
+      std::vector<NsTile> keep, moved;
+      for (size_t i = n; i-- > 0;) {
+        if (moved.size() < rem && v[i].tm < v[i].tn) moved.push_back(v[i]);
+        else keep.push_back(v[i]);
+      }
+      if (moved.size() < rem) continue;
+      std::reverse(keep.begin(), keep.end());
+      v.swap(keep);
+      for (auto it = moved.rbegin(); it != moved.rend(); ++it)
+        for (int i = 0; i < 2; ++i)
+          for (int j = 0; j < 2; ++j)
+            p.ns_tiles[ln][st][0].push_back({it->group, it->b, 2 * it->tm + i, 2 * it->tn + j});
+    }
   for (int ln = 0; ln < p.n_lanes; ++ln)
     for (int st = 0; st < 3; ++st)
       for (int sz = 0; sz < 2; ++sz) {
