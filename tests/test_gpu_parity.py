@@ -326,6 +326,27 @@ def test_update_step_parity_long_k_units(policy):
     say(f"  worst NS rel-Frobenius {worst:.3e}")
 
 
+@pytest.mark.timeout(600)
+def test_update_step_parity_longest_edge():
+    """Muon units at the longest edge a plan accepts (c = 4194176), wide and
+    tall, with r = 2 and 4: one 128-tile Gram per unit over K = 4194176 from
+    X^T (its buffer resource at the 32-bit offset limit), B as a bf16 pair,
+    32767 update tiles, G over 131068 blocks a row; against the float64 oracle."""
+    wl = workloads.longest_edge_units()
+    say(f"update_step {wl.name}")
+    st = DeviceState(wl)
+    gs = st.plan.groups()
+    assert [(g["c_pad"], g["gram_kmajor"], g["split_b"]) for g in gs] == [(4194176, 1, 1)] * 2
+    w0, g = wl.arrays()
+    st.step(1)
+    h = st.host()
+    z = np.zeros_like(w0)
+    say("  float64 oracle on the host ...")
+    ref, dirs = oracle_step(wl, wl.scale_layout, w0, g, z, z, 1)
+    worst = check_step(wl, wl.scale_layout, h, ref, dirs, w0)
+    say(f"  worst NS rel-Frobenius {worst:.3e}")
+
+
 @pytest.mark.parametrize("cid", [102, 103, 104])
 def test_update_step_parity_random_shapes(cid):
     """Seeded random unit shapes, with 256-tiles wherever a 256-aligned block

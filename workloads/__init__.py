@@ -228,6 +228,18 @@ def long_k_units(cid=105, name="4096 x 4224 wide and 4224 x 4096 tall Muon units
     return _finish(cid, name, t, "tile32x4")
 
 
+def longest_edge_units(cid=106, name="2 x 4194176 wide and 4194176 x 4 tall Muon units"):
+    """Muon units at the longest edge the library takes (4194176, the largest
+    multiple of 128 whose 256-row operand panels stay within 32-bit byte
+    offsets), wide (quantised) and tall, beside an AdamW vector: the Gram then
+    runs one 128-tile per unit over K = 4194176 and the update 32767 tiles."""
+    t = _Tree()
+    t.region(2, 4194176, unit=True, opt="muon", quant=True)
+    t.region(4194176, 4, unit=True, opt="muon")
+    t.region(1, 4096, unit=True, opt="adamw")
+    return _finish(cid, name, t, "rowmajor")
+
+
 def random_units(cid=102, n=6, name="random Muon shapes"):
     """n Muon units of random shapes (rows, cols in [2, 640], cols a multiple
     of 4, drawn on the structure stream), wide and tall, each its own region,
