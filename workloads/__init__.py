@@ -183,7 +183,8 @@ def flat_shard(cid, name, total, lo=4096, hi=50_000_000, frac2d=0.9,
 def ragged_mix(cid=100, name="ragged mix (odd shapes, strided views)"):
     """Small mixed tree whose shapes span several tiles with ragged tails:
     wide and tall Muon units not multiple of any tile, strided column views
-    (per-head slices of an output projection), and odd-length AdamW vectors."""
+    (per-head slices of an output projection), odd-length AdamW vectors, and a
+    Muon and an AdamW unit whose gradient is exactly zero."""
     t = _Tree()
     qkv = t.region(6 * 48, 160, quant=True)                      # 6 heads of 48 x 160
     for h in range(6):
@@ -198,8 +199,10 @@ def ragged_mix(cid=100, name="ragged mix (odd shapes, strided views)"):
     s = t.region(5, 48)                                          # strided AdamW column view
     t.node(s, 8, 5, 20, unit=True, opt="adamw", row_stride=48)
     t.region(40, 64, unit=True, opt="muon", quant=True)          # 40 x 64 zero-grad unit
+    zmuon = len(t.nodes) - 1
+    t.region(2, 96, unit=True, opt="adamw", quant=True)          # zero-grad AdamW unit (decay only, G fused)
     wl = _finish(cid, name, t, "rowmajor")
-    wl.zero_grad_units = [len(t.nodes) - 1]
+    wl.zero_grad_units = [zmuon, len(t.nodes) - 1]
     return wl
 
 
