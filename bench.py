@@ -85,12 +85,18 @@ def parse():
 
 
 def source_digest(names):
-    """sha256 over the kernel sources a counter figure was taken on."""
+    """sha256 over the code of the kernel sources a counter figure was taken on:
+    comments and blank space are left out, so an edited comment keeps the
+    figure while any change to the code drops it."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "mxfp8_weight_repack_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "mxfp8_weight_repack_amd", "csrc", n)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)          # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                        # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
