@@ -326,6 +326,36 @@ def test_update_step_parity_long_k_units(policy):
     say(f"  worst NS rel-Frobenius {worst:.3e}")
 
 
+@pytest.mark.parametrize("case", ["c2s", "c3s", "ragged"])
+def test_ns_executed_counts_only_nonzero_units(case):
+    """sshdp_ns_executed after a step: per group, the Muon units whose gradient
+    (hence momentum, from zero) is not all zero, and the MFMA flops their tiles
+    ran -- all of the plan's tile flops when no unit is zero (the d=2048 twin),
+    that total scaled by the share of live units for the one-group MoE bank
+    (2 of 8 experts with zero gradient), less than it for the ragged mix."""
+    wl = _wl(case)
+    say(f"ns_executed {wl.name}")
+    st = DeviceState(wl)
+    st.step(1)
+    units, flops = st.plan.ns_executed(st.ws, st.ws_bytes, st.stream())
+    groups = st.plan.groups()
+    live = [0] * len(groups)
+    zero = set(wl.zero_grad_units)
+    for i, n in enumerate(wl.nodes):
+        if n["is_unit"] and n["optimizer"] == "muon" and i not in zero:
+            live[st.plan.node(i)[1]] += 1
+    assert units == live, (units, live)
+    total = st.plan.stats()["ns_tile_flops"]
+    if case == "c2s":
+        assert flops == pytest.approx(total, rel=1e-12)
+    elif case == "c3s":
+        (gi,) = groups
+        assert units[0] == gi["n_units"] - 6
+        assert flops == pytest.approx(total * units[0] / gi["n_units"], rel=1e-12)
+    else:
+        assert 0 < flops < total
+
+
 @pytest.mark.timeout(600)
 def test_update_step_parity_longest_edge():
     """Muon units at the longest edge a plan accepts (c = 4194176), wide and
