@@ -356,6 +356,36 @@ def test_ns_executed_counts_only_nonzero_units(case):
         assert 0 < flops < total
 
 
+def test_profiling_brackets_kernel_classes_without_changing_results():
+    """sshdp_profile_enable/_read on the d=2048 twin: a profiled step gives the
+    same bits as an unprofiled one; every class the step runs reports launches
+    and time; the Newton-Schulz window (fork to join) is at least the sum of the
+    launch stream's Gram, poly and update launches inside it; a read resets the
+    counts, and a step with profiling off records nothing."""
+    wl = workloads.config(2, small=True)
+    say(f"profiling {wl.name}")
+    a, b = DeviceState(wl), DeviceState(wl)
+    a.plan.profile(True)
+    a.step(1)
+    b.step(1)
+    ha, hb = a.host(), b.host()
+    for k in ha:
+        assert np.array_equal(ha[k], hb[k]), k
+    prof = a.plan.profile_read()
+    for c in ("momentum", "norm", "ns_gram", "ns_poly", "ns_update", "ns_phase", "requant", "adamw",
+              "lane0_gram", "lane0_poly", "lane0_update", "lane0_update_last"):
+        ms, n = prof[c]
+        assert n > 0 and ms > 0.0, (c, prof[c])
+    assert prof["ns_phase"][1] == 1 and prof["lane0_update_last"][1] == 1
+    lane0 = sum(prof[c][0] for c in ("lane0_gram", "lane0_poly", "lane0_update", "lane0_update_last"))
+    assert prof["ns_phase"][0] >= lane0 * (1 - 1e-3), prof
+    assert all(n == 0 and ms == 0.0 for ms, n in a.plan.profile_read().values())
+    a.plan.profile(False)
+    a.step(2)
+    a.host()
+    assert all(n == 0 for _, n in a.plan.profile_read().values())
+
+
 @pytest.mark.timeout(600)
 def test_update_step_parity_longest_edge():
     """Muon units at the longest edge a plan accepts (c = 4194176), wide and
