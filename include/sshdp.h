@@ -381,14 +381,15 @@ int sshdp_ns_executed(const sshdp_plan *plan, const void *workspace, size_t work
 
 /* Per-stage kernel timing for benchmarking: when enabled on a plan, launching
  * calls bracket each kernel class with HIP events on the launch stream and
- * accumulate durations (milliseconds) and launch counts; reading synchronises
- * on those events.  Classes: 0 momentum (f0), 1 norm, 2 NS Gram, 3 NS poly,
+ * accumulate durations (milliseconds) and bracket counts; reading synchronises
+ * on those events, returns the sums since the previous read and clears them.
+ * Classes: 0 momentum (f0), 1 norm, 2 NS Gram, 3 NS poly,
  * 4 NS update (+f2), 5 AdamW, 6 AdamW+G fused, 7 G requant, 8 the whole
  * Newton-Schulz phase on the caller's stream (fork to join: NS launches of
  * different groups run concurrently on plan-owned streams, so classes 2-4 can
  * overlap in time), 9 G bf16 cast, and the Newton-Schulz launches of the
- * caller's stream alone (the groups whose sshdp_group_info.lane is 0): 10 Gram,
- * 11 poly (both tile sizes), 12 the update's 256-tile launch in the steps
+ * caller's stream alone (the groups whose sshdp_group_info.lane is 0): 10 Gram
+ * and 11 poly (both tile sizes), 12 the update's 256-tile launch in the steps
  * before the last, 13 that launch in the last step (+f2).
  * Not thread-safe; for measurement only. */
 enum { SSHDP_PROF_CLASSES = 14 };
