@@ -138,20 +138,46 @@ __global__ __launch_bounds__(256) void k_f0(const MuonUnit *__restrict__ units, 
 }
 
 // ----------------------------------------------------------------------------- norm
-__global__ __launch_bounds__(256) void k_norm(const MuonUnit *__restrict__ units, const int32_t *__restrict__ ulist,
-                                              const float *__restrict__ partials, float *__restrict__ uscale,
-                                              float eps) {
-  __shared__ float red[4];
+// One workgroup per unit sums the unit's f0 partials in a fixed order: thread t
+// keeps kNormUnroll running sums (partials t + kNormThreads*(kNormUnroll*j + k)),
+// so each thread has that many loads in flight, then the sums, the wave
+// butterfly and the waves are combined in order (bit-reproducible).
+constexpr int kNormThreads = 1024, kNormUnroll = 8;
+__global__ __launch_bounds__(kNormThreads) void k_norm(const MuonUnit *__restrict__ units,
+                                                       const int32_t *__restrict__ ulist,
+                                                       const float *__restrict__ partials,
+                                                       float *__restrict__ uscale, float eps) {
+  constexpr int NW = kNormThreads / 64;
+  __shared__ float red[NW];
   const int32_t ui = ulist[blockIdx.x];
   const MuonUnit u = units[ui];
-  float s = 0.f;
-  for (int i = u.tile_begin + threadIdx.x; i < u.tile_end; i += 256) s += partials[i];
+  const int t = threadIdx.x, n = u.tile_end - u.tile_begin;
+  const float *pp = partials + u.tile_begin;
+  float acc[kNormUnroll];
+#pragma unroll
+  for (int k = 0; k < kNormUnroll; ++k) acc[k] = 0.f;
+  for (int base = 0; base < n; base += kNormThreads * kNormUnroll) {
+#pragma unroll
+    for (int k = 0; k < kNormUnroll; ++k) {
+      const int i = base + k * kNormThreads + t;
+      if (i < n) acc[k] += pp[i];
+    }
+  }
+#pragma unroll
+  for (int w = kNormUnroll / 2; w >= 1; w >>= 1)
+#pragma unroll
+    for (int k = 0; k < w; ++k) acc[k] = acc[2 * k] + acc[2 * k + 1];
+  float s = acc[0];
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  if ((t & 63) == 0) red[t >> 6] = s;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  if (t == 0) {
+#pragma unroll
+    for (int w = NW / 2; w >= 1; w >>= 1)
+#pragma unroll
+      for (int k = 0; k < w; ++k) red[k] = red[2 * k] + red[2 * k + 1];
+    const float tot = red[0];
     // an all-zero unit gets scale 0: its Newton-Schulz products are skipped (direction exactly 0)
     uscale[ui] = tot > 0.f ? 1.0f / (sqrtf(tot) + eps) : 0.f;
   }
@@ -433,7 +459,7 @@ hipError_t launch_f0(const sshdp_plan &p, int lane, const float *g, float *m, fl
 hipError_t launch_norm(const sshdp_plan &p, int lane, char *ws, float eps, hipStream_t s) {
   const int32_t b = p.norm_lane[lane], n = p.norm_lane[lane + 1] - b;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_norm, dim3((unsigned)n), dim3(256), 0, s, p.d.munits, p.d.norm_units + b,
+  hipLaunchKernelGGL(k_norm, dim3((unsigned)n), dim3(kNormThreads), 0, s, p.d.munits, p.d.norm_units + b,
                      reinterpret_cast<const float *>(ws + p.ws_partials), reinterpret_cast<float *>(ws + p.ws_uscale),
                      eps);
   return hipGetLastError();
